@@ -1,0 +1,241 @@
+/*
+ * gdn_paged.h -- Gated Delta-Rule prefill and decode on a paged recurrent-state
+ * pool, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Semantics follow the flashinfer.gdn_paged API page (docs.flashinfer.ai,
+ * "flashinfer.gdn_paged"): its opening paragraph, the "Page table" section and
+ * the "Slot arguments of chunk_gated_delta_rule" section.  The page names the
+ * Gated Delta-Rule without writing it out; this library computes, per v-head,
+ * with a state S of shape [V, K]:
+ *
+ *     alpha_t = exp(g_t)
+ *     S_t     = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T
+ *     o_t     = scale * S_t q_t           (scale = 1/sqrt(K) unless given)
+ *
+ * Data layout (row-major, all device memory, all owned by the caller):
+ *   q, k         [T, Hqk, K]  bf16 (raw 16-bit patterns)
+ *   v            [T, H, V]    bf16
+ *   g, beta      [T, H]       fp32 (either may be NULL: g = 0, beta = 1)
+ *   o            [T, H, V]    bf16, written for every new token
+ *   state pools  [rows, H, V, K] fp32; each row is one dense [H, V, K] block and
+ *                consecutive rows sit `row_stride` floats apart (>= H*V*K).
+ * Decode uses B (one token per sequence) in place of T.
+ * v-head h reads q/k head h / (H / Hqk).
+ *
+ * Calls are asynchronous on `stream`, never synchronize with the host and
+ * allocate nothing: the caller passes a workspace where one is needed
+ * (gdn_prefill_workspace_size).  Return value: GDN_OK or a negative status,
+ * set before any launch for every check the host can make; the message is in
+ * gdn_last_error() (thread-local).  Device-side contents are NOT validated
+ * (the page says slots are not checked against the page table): page ids must
+ * be real rows of the pool, decode sequences must hold a token before the
+ * decoded one, and rows one sequence writes must be neither read nor written
+ * by another sequence of the same call.  Breaking these is undefined
+ * behaviour.
+ *
+ * Supported: K = V = 128, H a multiple of Hqk, page_size and
+ * checkpoint_every_n_tokens positive multiples of 64.
+ */
+#ifndef GDN_PAGED_H
+#define GDN_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,        /* bad argument (null pointer, size, missing companion) */
+  GDN_EUNSUPPORTED = -2,  /* valid per the page but not served by this build */
+  GDN_ELAUNCH = -3,       /* a kernel launch failed */
+  GDN_EWORKSPACE = -4     /* workspace missing or too small */
+};
+
+enum { GDN_INDEX_INT32 = 0, GDN_INDEX_INT64 = 1 };
+
+/* Head geometry shared by every call. */
+typedef struct {
+  int32_t num_qk_heads; /* Hqk */
+  int32_t num_v_heads;  /* H, also the pool's head count */
+  int32_t head_dim_k;   /* K, must be 128 */
+  int32_t head_dim_v;   /* V, must be 128 */
+  float scale;          /* output scale; <= 0 selects 1/sqrt(K) */
+} gdn_dims_t;
+
+/*
+ * Per-sequence pool rows of a paged prefill batch, each a device array of
+ * [num_seqs] int32 (flashinfer.gdn_paged, GDNPagedPrefillSlots: "all
+ * [num_seqs] int32"; the page names state_indices, the other fields are this
+ * library's reading of the thin-wrapper description):
+ *   state_indices         page holding the last prefix token, -1 if no prefix
+ *   output_state_indices  last page, -1 for a sequence with no new tokens
+ *   checkpoint_cu_starts  indptr[b] + prefix / page_size: where the pages that
+ *                         end inside this call start in page_indices
+ *   prefix_lens           tokens the sequence held before the call
+ *   chunk_starts          exclusive prefix sum of 64-token chunk counts
+ *                         (chunks sit at absolute multiples of 64)
+ * The struct itself lives in host memory; its pointers are device pointers.
+ */
+typedef struct {
+  int32_t* state_indices;
+  int32_t* output_state_indices;
+  int32_t* checkpoint_cu_starts;
+  int32_t* prefix_lens;
+  int32_t* chunk_starts;
+} gdn_prefill_slots_t;
+
+/* Per-sequence pool rows of a paged decode batch, [num_seqs] int32 each
+ * (flashinfer.gdn_paged, GDNPagedDecodeSlots). */
+typedef struct {
+  int32_t* initial_state_indices;
+  int32_t* output_state_indices;
+} gdn_decode_slots_t;
+
+/*
+ * gdn_prefill_slots -- pool rows a paged prefill derives from its page table,
+ * in one launch and without a host synchronization (flashinfer.gdn_paged,
+ * gdn_paged_prefill_slots and "Page table").  The rows depend only on the
+ * batch: compute them once per step and pass them to every layer's
+ * gdn_prefill_paged, which then skips this launch.
+ *   cu_seqlens [num_seqs+1], page_indices [indptr[num_seqs]],
+ *   page_indptr [num_seqs+1], last_page_len [num_seqs]: int32 device arrays.
+ *   out: five [num_seqs] int32 device arrays, written.
+ * Errors: GDN_EINVAL for null pointers, num_seqs < 0, page_size not a positive
+ * multiple of 64.
+ */
+int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,
+                      const int32_t* page_indptr, const int32_t* last_page_len,
+                      int32_t num_seqs, int32_t page_size,
+                      const gdn_prefill_slots_t* out, hipStream_t stream);
+
+/*
+ * gdn_decode_slots -- decode rows (flashinfer.gdn_paged, gdn_paged_decode_slots):
+ * a token that opens a new page (last_page_len == 1) reads the previous page
+ * and writes the new one; otherwise both rows are the last page.
+ * Errors: GDN_EINVAL for null pointers or num_seqs < 0.
+ */
+int gdn_decode_slots(const int32_t* page_indices, const int32_t* page_indptr,
+                     const int32_t* last_page_len, int32_t num_seqs,
+                     const gdn_decode_slots_t* out, hipStream_t stream);
+
+/*
+ * Workspace bytes gdn_prefill_paged / gdn_prefill need for a batch of
+ * `total_tokens` new tokens in `num_seqs` sequences (an upper bound that
+ * depends on sizes only, so it can be sized once).  0 on bad dims.
+ */
+size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                  const gdn_dims_t* dims);
+
+/*
+ * gdn_prefill_paged -- chunked prefill that reads and writes a paged pool
+ * (flashinfer.gdn_paged, chunk_gated_delta_rule_paged and "Page table"):
+ *  - the initial state is the page holding the last prefix token, or zero
+ *    when the prefix is empty;
+ *  - the state at every page boundary the new tokens cross goes to the page
+ *    ending there, and the final state to the last page;
+ *  - pages that end at or before the prefix are never written; a prefix that
+ *    ends inside a page continues that page in place;
+ *  - prefixes need not be multiples of 64 (the first chunk is padded on the
+ *    left); zero-length sequences leave the pool unchanged.
+ * Sequence b owns pages page_indices[page_indptr[b] .. page_indptr[b+1]) and
+ * holds (pages-1)*page_size + last_page_len[b] tokens after the call; its new
+ * tokens are q/k/v rows cu_seqlens[b] .. cu_seqlens[b+1].
+ *   slots: NULL, or rows from gdn_prefill_slots for this batch (not checked).
+ *   total_tokens = cu_seqlens[num_seqs] (host copy; sizes the launch grids).
+ *   workspace: >= gdn_prefill_workspace_size(total_tokens, num_seqs, dims)
+ *   bytes of device memory, 256-byte aligned, contents scratch.
+ * Errors: GDN_EINVAL (null pointer, negative size, page_size not a positive
+ * multiple of 64, pool_row_stride < H*V*K), GDN_EUNSUPPORTED (K or V != 128,
+ * H not a multiple of Hqk), GDN_EWORKSPACE, GDN_ELAUNCH.
+ */
+int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const int32_t* cu_seqlens,
+                      int32_t num_seqs, int64_t total_tokens, float* state_pool,
+                      int64_t pool_row_stride, const int32_t* page_indices,
+                      const int32_t* page_indptr, const int32_t* last_page_len,
+                      int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_decode_paged -- one token per sequence on a paged pool (flashinfer.gdn_paged,
+ * gated_delta_rule_decode_paged): last_page_len[b] == 1 reads page n-2 and
+ * writes page n-1, otherwise the last page is updated in place.  Every
+ * sequence holds at least one token before the decoded one.
+ *   q, k [num_seqs, Hqk, K], v [num_seqs, H, V], g, beta [num_seqs, H], o
+ *   [num_seqs, H, V].  slots: NULL (rows are derived inside the decode
+ *   kernel, no extra launch) or rows from gdn_decode_slots.
+ * Errors as gdn_prefill_paged (no workspace is needed).
+ */
+int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                     const float* g, const float* beta, int32_t num_seqs, float* state_pool,
+                     int64_t pool_row_stride, const int32_t* page_indices,
+                     const int32_t* page_indptr, const int32_t* last_page_len,
+                     int32_t page_size, const gdn_decode_slots_t* slots, void* o,
+                     hipStream_t stream);
+
+/*
+ * gdn_prefill -- the slot-argument prefill that the paged call wraps
+ * (flashinfer.gdn_paged, "Slot arguments of chunk_gated_delta_rule").
+ *   initial_state [rows, H, V, K] or NULL (all sequences start from zero);
+ *   state_indices: read row per sequence (-1 = zero state); NULL = row b.
+ *   output_final_state: store final states into output_state;
+ *   output_state_indices: write row per sequence (-1 = skip); NULL = the read
+ *     row (state_indices[b], or b).  Needs output_state and
+ *     output_final_state.  A zero-length sequence writes nothing.
+ *   state_checkpoints + checkpoint_state_indices + checkpoint_cu_starts +
+ *     prefix_lens + checkpoint_every_n_tokens (N): after new token n of
+ *     sequence i with (prefix_lens[i] + n) % N == 0, the state goes to row
+ *     checkpoint_state_indices[checkpoint_cu_starts[i] + j] (j counts the
+ *     call's checkpoints from 0; -1 skips).  Sequence i takes
+ *     (prefix_lens[i] + len_i)/N - prefix_lens[i]/N checkpoints.
+ *   prefix_lens alone (no checkpoints) only aligns chunks; results match.
+ *   index_dtype: GDN_INDEX_INT32 or GDN_INDEX_INT64 for state_indices,
+ *     output_state_indices, checkpoint_state_indices, checkpoint_cu_starts and
+ *     prefix_lens.  cu_seqlens is always int32.
+ *   The three state buffers may be the same memory.
+ * Errors: GDN_EINVAL (as above; output_state_indices without output_state or
+ * output_final_state; checkpoint rows without N > 0, prefix_lens,
+ * checkpoint_cu_starts or state_checkpoints), GDN_EUNSUPPORTED (N not a
+ * multiple of 64, K or V != 128), GDN_EWORKSPACE, GDN_ELAUNCH.
+ */
+int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, const int32_t* cu_seqlens,
+                int32_t num_seqs, int64_t total_tokens,
+                const float* initial_state, int64_t initial_row_stride,
+                const void* state_indices,
+                float* output_state, int64_t output_row_stride,
+                const void* output_state_indices, int32_t output_final_state,
+                float* state_checkpoints, int64_t checkpoint_row_stride,
+                const void* checkpoint_state_indices, const void* checkpoint_cu_starts,
+                const void* prefix_lens, int32_t checkpoint_every_n_tokens,
+                int32_t index_dtype, void* o, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * gdn_decode -- single-token step with explicit rows (the decode counterpart
+ * of the slot arguments).  initial_state NULL or a read row of -1 starts from
+ * zero; initial_state_indices NULL = row b; output_state_indices NULL = the
+ * read row; a write row of -1 skips the store.
+ */
+int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+               const float* g, const float* beta, int32_t num_seqs,
+               const float* initial_state, int64_t initial_row_stride,
+               const void* initial_state_indices, float* output_state,
+               int64_t output_row_stride, const void* output_state_indices,
+               int32_t index_dtype, void* o, hipStream_t stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+/* Library version string. */
+const char* gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_PAGED_H */

@@ -96,17 +96,26 @@ def _head_map(H: int, Hqk: int) -> np.ndarray:
     return np.arange(H) // (H // Hqk)
 
 
-def _check_hazards(read_rows: Dict[int, int], write_rows: Dict[int, set]):
-    """Rows one sequence writes are read or written by no other sequence."""
-    owner = {}
-    for b, rows in write_rows.items():
-        for r in rows:
-            if r in owner and owner[r] != b:
-                raise ValueError(f"row {r} written by sequences {owner[r]} and {b}")
-            owner[r] = b
-    for b, r in read_rows.items():
-        if r in owner and owner[r] != b:
-            raise ValueError(f"row {r} read by sequence {b} but written by {owner[r]}")
+def _check_hazards(reads: Dict[int, int], final_w: Dict[int, set], ckpt_w: Dict[int, set],
+                   shared_pool: bool):
+    """Rows one sequence writes are read or written by no other sequence.
+
+    With ``shared_pool`` the initial, output and checkpoint buffers are one
+    memory (the paged case); otherwise each buffer is checked on its own and
+    reads (of the initial buffer) cannot collide with writes."""
+    groups = [(final_w, ckpt_w)] if shared_pool else [(final_w,), (ckpt_w,)]
+    for grp in groups:
+        owner = {}
+        for w in grp:
+            for b, rows in w.items():
+                for r in rows:
+                    if r in owner and owner[r] != b:
+                        raise ValueError(f"row {r} written by sequences {owner[r]} and {b}")
+                    owner[r] = b
+        if shared_pool:
+            for b, r in reads.items():
+                if r in owner and owner[r] != b:
+                    raise ValueError(f"row {r} read by sequence {b} but written by {owner[r]}")
 
 
 def prefill(q, k, v, g, beta, cu_seqlens, *,
@@ -114,14 +123,16 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
             output_final_state: bool = False, output_state_indices=None,
             checkpoint_state_indices=None, checkpoint_cu_starts=None,
             prefix_lens=None, checkpoint_every_n_tokens: int = 0,
-            scale: Optional[float] = None) -> Result:
+            scale: Optional[float] = None, shared_pool: bool = True) -> Result:
     """General slot-argument prefill over a packed variable-length batch.
 
     q, k: [T, Hqk, K]; v: [T, H, V]; g, beta: [T, H] or None;
-    cu_seqlens: [B + 1]; initial_state: [rows, H, V, K] or None.
+    cu_seqlens: [B + 1]; initial_state: [rows, H, V, K] (anything indexable by
+    row) or None.
     Without ``state_indices`` sequence ``b`` reads row ``b`` of
     ``initial_state``; without ``output_state_indices`` it writes back to its
-    read row (an in-place slot update).
+    read row (an in-place slot update).  ``shared_pool`` says whether the
+    three state buffers are one memory (for the cross-sequence hazard check).
     """
     q, k, v = _f64(_to_numpy(q)), _f64(_to_numpy(k)), _f64(_to_numpy(v))
     T, Hqk, K = q.shape
@@ -133,7 +144,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
     hmap = _head_map(H, Hqk)
     if scale is None:
         scale = 1.0 / math.sqrt(K)
-    init = _to_numpy(initial_state)
+    init = initial_state  # indexed row by row: ndarray, tensor or any row-indexable object
     sidx = None if state_indices is None else [int(x) for x in _to_numpy(state_indices)]
     oidx = None if output_state_indices is None else [int(x) for x in _to_numpy(output_state_indices)]
     N = int(checkpoint_every_n_tokens)
@@ -147,7 +158,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
         raise ValueError("output_state_indices needs output_final_state")
 
     res = Result(o=np.zeros((T, H, V)))
-    reads, writes = {}, {}
+    reads, final_w, ckpt_w = {}, {}, {}
     for b in range(B):
         L = cu[b + 1] - cu[b]
         if L == 0:
@@ -159,7 +170,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
         if rd == -1:
             S = np.zeros((H, V, K))
         else:
-            S = _f64(init[rd]).copy()
+            S = _f64(_to_numpy(init[rd])).copy()
             reads[b] = rd
         res.reads[b] = rd
         p = plen[b] if plen is not None else 0
@@ -171,7 +182,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
                 row = cidx[cstart[b] + j]
                 if row != -1:
                     res.checkpoints[row] = S.copy()
-                    writes.setdefault(b, set()).add(row)
+                    ckpt_w.setdefault(b, set()).add(row)
         if output_final_state:
             if oidx is not None:
                 wr = oidx[b]
@@ -179,13 +190,14 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
                 wr = sidx[b] if sidx is not None else b
             if wr != -1:
                 res.final[wr] = S.copy()
-                writes.setdefault(b, set()).add(wr)
-    _check_hazards(reads, writes)
+                final_w.setdefault(b, set()).add(wr)
+    _check_hazards(reads, final_w, ckpt_w, shared_pool)
     return res
 
 
 def decode(q, k, v, g, beta, *, initial_state, initial_state_indices=None,
-           output_state_indices=None, scale: Optional[float] = None) -> Result:
+           output_state_indices=None, scale: Optional[float] = None,
+           shared_pool: bool = True) -> Result:
     """One token per sequence.  q, k: [B, Hqk, K]; v: [B, H, V]; g, beta: [B, H].
 
     Rows default to ``b``; the write row defaults to the read row.  A read row
@@ -198,7 +210,7 @@ def decode(q, k, v, g, beta, *, initial_state, initial_state_indices=None,
     widx = ridx if output_state_indices is None else output_state_indices
     return prefill(q, k, v, g, beta, cu, initial_state=initial_state,
                    state_indices=ridx, output_final_state=True,
-                   output_state_indices=widx, scale=scale)
+                   output_state_indices=widx, scale=scale, shared_pool=shared_pool)
 
 
 def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_indptr,

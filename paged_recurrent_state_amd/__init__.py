@@ -1,0 +1,22 @@
+"""Gated Delta-Rule prefill and decode on a paged recurrent-state pool, MI355X (gfx950).
+
+The compute runs in hand-written HIP kernels in ``libgdn_paged.so`` (C ABI:
+``include/gdn_paged.h``); this package only marshals torch tensors into it.
+Build the library with ``python -m paged_recurrent_state_amd.build``.
+"""
+
+from ._lib import (  # noqa: F401
+    DecodeSlots,
+    GDNError,
+    PrefillSlots,
+    decode,
+    decode_paged,
+    decode_slots,
+    load,
+    lib_path,
+    prefill,
+    prefill_paged,
+    prefill_slots,
+    prefill_workspace_size,
+    version,
+)

@@ -1,0 +1,408 @@
+// C-ABI entry points: argument checks, workspace carving and launches.
+// Every host-checkable error returns before any launch; nothing here
+// synchronizes with the device or allocates memory.
+#include "gdn_paged.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return GDN_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDN_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return GDN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  int64_t nc;  // chunk slots: >= sum over sequences of ceil(((p mod 64) + L) / 64)
+  size_t slots, T, P, scal, Kt, total;
+};
+
+WsLayout ws_layout(int64_t T, int B, int H, int Hqk) {
+  WsLayout w;
+  // ceil((r + L) / 64) with r < 64 is at most (L + 126) / 64, so the chunks of
+  // a batch never exceed T / 64 + 2 B.
+  w.nc = T / kChunk + 2 * (int64_t)B + 1;
+  size_t off = 0;
+  w.slots = off;
+  off += align256((size_t)5 * B * sizeof(int32_t));
+  w.T = off;
+  off += align256((size_t)w.nc * H * kMatWords * sizeof(u16));
+  w.P = off;
+  off += align256((size_t)w.nc * H * kMatWords * sizeof(u16));
+  w.scal = off;
+  off += align256((size_t)w.nc * H * kScal * sizeof(float));
+  w.Kt = off;
+  off += align256((size_t)w.nc * Hqk * kKtWords * sizeof(u16));
+  w.total = off;
+  return w;
+}
+
+int check_dims(const gdn_dims_t* d) {
+  if (!d) return fail(GDN_EINVAL, "dims is NULL");
+  if (d->num_qk_heads <= 0 || d->num_v_heads <= 0)
+    return fail(GDN_EINVAL, "head counts must be positive (Hqk=%d, H=%d)", d->num_qk_heads,
+                d->num_v_heads);
+  if (d->head_dim_k != kDim || d->head_dim_v != kDim)
+    return fail(GDN_EUNSUPPORTED, "only K = V = 128 is built (K=%d, V=%d)", d->head_dim_k,
+                d->head_dim_v);
+  if (d->num_v_heads % d->num_qk_heads != 0)
+    return fail(GDN_EUNSUPPORTED, "v-heads (%d) must be a multiple of q/k heads (%d)",
+                d->num_v_heads, d->num_qk_heads);
+  return GDN_OK;
+}
+
+float eff_scale(const gdn_dims_t* d) {
+  return d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim_k);
+}
+
+int64_t state_block(const gdn_dims_t* d) { return (int64_t)d->num_v_heads * kDim * kDim; }
+
+int check_tokens(const void* q, const void* k, const void* v, const int32_t* cu, const void* o) {
+  if (!q || !k || !v) return fail(GDN_EINVAL, "q, k and v must not be NULL");
+  if (!cu) return fail(GDN_EINVAL, "cu_seqlens must not be NULL");
+  if (!o) return fail(GDN_EINVAL, "o must not be NULL");
+  return GDN_OK;
+}
+
+int check_page_size(int32_t ps) {
+  if (ps <= 0 || ps % kChunk != 0)
+    return fail(GDN_EINVAL, "page_size must be a positive multiple of 64 (got %d)", ps);
+  return GDN_OK;
+}
+
+SlotsDev carve_slots(void* ws, const WsLayout& L, int B) {
+  int32_t* base = (int32_t*)((char*)ws + L.slots);
+  return SlotsDev{base, base + B, base + 2 * B, base + 3 * B, base + 4 * B};
+}
+
+ChunkWs carve_chunk(void* ws, const WsLayout& L) {
+  char* w = (char*)ws;
+  return ChunkWs{(u16*)(w + L.T), (u16*)(w + L.P), (float*)(w + L.scal), (u16*)(w + L.Kt)};
+}
+
+// Launch the intra-chunk and recurrence kernels once the rows are on the device.
+int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, const int32_t* cu, int B,
+                const SlotsDev& sd, const WsLayout& L, void* ws, const float* init,
+                int64_t init_stride, float* out, int64_t out_stride, float* ckpt,
+                int64_t ckpt_stride, const void* ckpt_idx, int ckpt_idx64, int ckpt_every,
+                void* o, hipStream_t stream) {
+  ChunkParams cp;
+  cp.q = (const u16*)q;
+  cp.k = (const u16*)k;
+  cp.g = g;
+  cp.beta = beta;
+  cp.cu_seqlens = cu;
+  cp.slots = sd;
+  cp.num_seqs = B;
+  cp.H = d->num_v_heads;
+  cp.Hqk = d->num_qk_heads;
+  cp.group = d->num_v_heads / d->num_qk_heads;
+  cp.ws = carve_chunk(ws, L);
+  int rc = launched(launch_chunk(cp, L.nc, stream), "intra-chunk kernel");
+  if (rc) return rc;
+
+  RecurParams rp;
+  rp.q = (const u16*)q;
+  rp.k = (const u16*)k;
+  rp.v = (const u16*)v;
+  rp.o = (u16*)o;
+  rp.cu_seqlens = cu;
+  rp.slots = sd;
+  rp.num_seqs = B;
+  rp.H = d->num_v_heads;
+  rp.Hqk = d->num_qk_heads;
+  rp.group = d->num_v_heads / d->num_qk_heads;
+  rp.scale = eff_scale(d);
+  rp.init = init;
+  rp.init_stride = init_stride;
+  rp.out = out;
+  rp.out_stride = out_stride;
+  rp.ckpt = ckpt;
+  rp.ckpt_stride = ckpt_stride;
+  rp.ckpt_idx = ckpt_idx;
+  rp.ckpt_idx64 = ckpt_idx64;
+  rp.ckpt_every = ckpt_every;
+  rp.ws = cp.ws;
+  rc = launched(launch_recur(rp, stream), "recurrence kernel");
+  if (rc) return rc;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err.c_str(); }
+
+const char* gdn_version(void) { return "gdn_paged 0.1.0 (gfx950)"; }
+
+size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, const gdn_dims_t* dims) {
+  if (check_dims(dims) != GDN_OK || total_tokens < 0 || num_seqs < 0) return 0;
+  return ws_layout(total_tokens, num_seqs, dims->num_v_heads, dims->num_qk_heads).total;
+}
+
+int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,
+                      const int32_t* page_indptr, const int32_t* last_page_len,
+                      int32_t num_seqs, int32_t page_size, const gdn_prefill_slots_t* out,
+                      hipStream_t stream) {
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (int rc = check_page_size(page_size)) return rc;
+  if (!cu_seqlens || !page_indices || !page_indptr || !last_page_len)
+    return fail(GDN_EINVAL, "page table and cu_seqlens must not be NULL");
+  if (!out || !out->state_indices || !out->output_state_indices || !out->checkpoint_cu_starts ||
+      !out->prefix_lens || !out->chunk_starts)
+    return fail(GDN_EINVAL, "every output slot array must be given");
+  if (int rc = launched(launch_prefill_slots(cu_seqlens, page_indices, page_indptr, last_page_len,
+                                             num_seqs, page_size, out->state_indices,
+                                             out->output_state_indices,
+                                             out->checkpoint_cu_starts, out->prefix_lens,
+                                             out->chunk_starts, stream),
+                        "prefill slot kernel"))
+    return rc;
+  return ok();
+}
+
+int gdn_decode_slots(const int32_t* page_indices, const int32_t* page_indptr,
+                     const int32_t* last_page_len, int32_t num_seqs,
+                     const gdn_decode_slots_t* out, hipStream_t stream) {
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (!page_indices || !page_indptr || !last_page_len)
+    return fail(GDN_EINVAL, "page table must not be NULL");
+  if (!out || !out->initial_state_indices || !out->output_state_indices)
+    return fail(GDN_EINVAL, "both output slot arrays must be given");
+  if (int rc = launched(launch_decode_slots(page_indices, page_indptr, last_page_len, num_seqs,
+                                            out->initial_state_indices,
+                                            out->output_state_indices, stream),
+                        "decode slot kernel"))
+    return rc;
+  return ok();
+}
+
+int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const int32_t* cu_seqlens,
+                      int32_t num_seqs, int64_t total_tokens, float* state_pool,
+                      int64_t pool_row_stride, const int32_t* page_indices,
+                      const int32_t* page_indptr, const int32_t* last_page_len,
+                      int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = check_dims(dims)) return rc;
+  if (num_seqs < 0 || total_tokens < 0)
+    return fail(GDN_EINVAL, "num_seqs and total_tokens must be >= 0");
+  if (int rc = check_page_size(page_size)) return rc;
+  if (!cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must not be NULL");
+  if (!state_pool) return fail(GDN_EINVAL, "state_pool must not be NULL");
+  if (!page_indices || !page_indptr || !last_page_len)
+    return fail(GDN_EINVAL, "page table must not be NULL");
+  if (pool_row_stride < state_block(dims))
+    return fail(GDN_EINVAL, "pool_row_stride %lld < H*V*K", (long long)pool_row_stride);
+  if (num_seqs == 0) return ok();
+  if (total_tokens > 0)
+    if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, dims->num_qk_heads);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
+    return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
+                workspace_bytes);
+  SlotsDev sd;
+  if (slots) {
+    if (!slots->state_indices || !slots->output_state_indices || !slots->checkpoint_cu_starts ||
+        !slots->prefix_lens || !slots->chunk_starts)
+      return fail(GDN_EINVAL, "every slot array must be given");
+    sd = SlotsDev{slots->state_indices, slots->output_state_indices, slots->checkpoint_cu_starts,
+                  slots->prefix_lens, slots->chunk_starts};
+  } else {
+    sd = carve_slots(workspace, L, num_seqs);
+    if (int rc = launched(launch_prefill_slots(cu_seqlens, page_indices, page_indptr,
+                                               last_page_len, num_seqs, page_size,
+                                               (int32_t*)sd.read, (int32_t*)sd.write,
+                                               (int32_t*)sd.ckpt_start, (int32_t*)sd.prefix,
+                                               (int32_t*)sd.chunk_start, stream),
+                          "prefill slot kernel"))
+      return rc;
+  }
+  if (total_tokens == 0) return ok();
+  // The paged call is the slot-argument call with one pool for all three
+  // buffers and a checkpoint every page_size tokens into page_indices.
+  return run_prefill(dims, q, k, v, g, beta, cu_seqlens, num_seqs, sd, L, workspace, state_pool,
+                     pool_row_stride, state_pool, pool_row_stride, state_pool, pool_row_stride,
+                     page_indices, 0, page_size, o, stream);
+}
+
+int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                     const float* g, const float* beta, int32_t num_seqs, float* state_pool,
+                     int64_t pool_row_stride, const int32_t* page_indices,
+                     const int32_t* page_indptr, const int32_t* last_page_len,
+                     int32_t page_size, const gdn_decode_slots_t* slots, void* o,
+                     hipStream_t stream) {
+  if (int rc = check_dims(dims)) return rc;
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0");
+  if (int rc = check_page_size(page_size)) return rc;
+  if (!state_pool) return fail(GDN_EINVAL, "state_pool must not be NULL");
+  if (pool_row_stride < state_block(dims))
+    return fail(GDN_EINVAL, "pool_row_stride %lld < H*V*K", (long long)pool_row_stride);
+  if (num_seqs == 0) return ok();
+  if (!q || !k || !v || !o) return fail(GDN_EINVAL, "q, k, v and o must not be NULL");
+  DecodeParams dp{};
+  dp.q = (const u16*)q;
+  dp.k = (const u16*)k;
+  dp.v = (const u16*)v;
+  dp.g = g;
+  dp.beta = beta;
+  dp.o = (u16*)o;
+  dp.num_seqs = num_seqs;
+  dp.H = dims->num_v_heads;
+  dp.Hqk = dims->num_qk_heads;
+  dp.group = dims->num_v_heads / dims->num_qk_heads;
+  dp.scale = eff_scale(dims);
+  dp.init = state_pool;
+  dp.init_stride = pool_row_stride;
+  dp.out = state_pool;
+  dp.out_stride = pool_row_stride;
+  if (slots) {
+    if (!slots->initial_state_indices || !slots->output_state_indices)
+      return fail(GDN_EINVAL, "both slot arrays must be given");
+    dp.mode = 0;
+    dp.rd_idx = slots->initial_state_indices;
+    dp.wr_idx = slots->output_state_indices;
+    dp.idx64 = 0;
+  } else {
+    if (!page_indices || !page_indptr || !last_page_len)
+      return fail(GDN_EINVAL, "page table must not be NULL");
+    dp.mode = 1;
+    dp.page_indices = page_indices;
+    dp.page_indptr = page_indptr;
+    dp.last_page_len = last_page_len;
+  }
+  if (int rc = launched(launch_decode(dp, stream), "decode kernel")) return rc;
+  return ok();
+}
+
+int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                const float* g, const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                int64_t total_tokens, const float* initial_state, int64_t initial_row_stride,
+                const void* state_indices, float* output_state, int64_t output_row_stride,
+                const void* output_state_indices, int32_t output_final_state,
+                float* state_checkpoints, int64_t checkpoint_row_stride,
+                const void* checkpoint_state_indices, const void* checkpoint_cu_starts,
+                const void* prefix_lens, int32_t checkpoint_every_n_tokens, int32_t index_dtype,
+                void* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int rc = check_dims(dims)) return rc;
+  if (num_seqs < 0 || total_tokens < 0)
+    return fail(GDN_EINVAL, "num_seqs and total_tokens must be >= 0");
+  if (!cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must not be NULL");
+  if (index_dtype != GDN_INDEX_INT32 && index_dtype != GDN_INDEX_INT64)
+    return fail(GDN_EINVAL, "index_dtype must be GDN_INDEX_INT32 or GDN_INDEX_INT64");
+  const int64_t blk = state_block(dims);
+  if (initial_state && initial_row_stride < blk)
+    return fail(GDN_EINVAL, "initial_row_stride < H*V*K");
+  if (output_state_indices && (!output_final_state || !output_state))
+    return fail(GDN_EINVAL,
+                "output_state_indices needs output_state and output_final_state");
+  if (output_final_state && !output_state)
+    return fail(GDN_EINVAL, "output_final_state needs output_state");
+  if (output_state && output_row_stride < blk)
+    return fail(GDN_EINVAL, "output_row_stride < H*V*K");
+  if (checkpoint_state_indices) {
+    if (checkpoint_every_n_tokens <= 0 || !prefix_lens || !checkpoint_cu_starts ||
+        !state_checkpoints)
+      return fail(GDN_EINVAL,
+                  "checkpoint_state_indices needs checkpoint_every_n_tokens > 0, prefix_lens, "
+                  "checkpoint_cu_starts and state_checkpoints");
+    if (checkpoint_every_n_tokens % kChunk != 0)
+      return fail(GDN_EUNSUPPORTED,
+                  "checkpoint_every_n_tokens must be a multiple of 64 (got %d)",
+                  checkpoint_every_n_tokens);
+    if (checkpoint_row_stride < blk) return fail(GDN_EINVAL, "checkpoint_row_stride < H*V*K");
+  }
+  if (num_seqs == 0 || total_tokens == 0) return ok();
+  if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, dims->num_qk_heads);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
+    return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
+                workspace_bytes);
+  const int idx64 = index_dtype == GDN_INDEX_INT64;
+  const SlotsDev sd = carve_slots(workspace, L, num_seqs);
+  if (int rc = launched(
+          launch_general_slots(cu_seqlens, num_seqs, state_indices, output_state_indices,
+                               checkpoint_state_indices ? checkpoint_cu_starts : nullptr,
+                               prefix_lens, idx64, initial_state != nullptr,
+                               output_final_state != 0, (int32_t*)sd.read, (int32_t*)sd.write,
+                               (int32_t*)sd.ckpt_start, (int32_t*)sd.prefix,
+                               (int32_t*)sd.chunk_start, stream),
+          "slot-argument kernel"))
+    return rc;
+  return run_prefill(dims, q, k, v, g, beta, cu_seqlens, num_seqs, sd, L, workspace,
+                     initial_state, initial_row_stride, output_state, output_row_stride,
+                     state_checkpoints, checkpoint_row_stride, checkpoint_state_indices, idx64,
+                     checkpoint_every_n_tokens, o, stream);
+}
+
+int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+               const float* g, const float* beta, int32_t num_seqs, const float* initial_state,
+               int64_t initial_row_stride, const void* initial_state_indices,
+               float* output_state, int64_t output_row_stride, const void* output_state_indices,
+               int32_t index_dtype, void* o, hipStream_t stream) {
+  if (int rc = check_dims(dims)) return rc;
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0");
+  if (index_dtype != GDN_INDEX_INT32 && index_dtype != GDN_INDEX_INT64)
+    return fail(GDN_EINVAL, "index_dtype must be GDN_INDEX_INT32 or GDN_INDEX_INT64");
+  const int64_t blk = state_block(dims);
+  if (initial_state && initial_row_stride < blk)
+    return fail(GDN_EINVAL, "initial_row_stride < H*V*K");
+  if (output_state && output_row_stride < blk)
+    return fail(GDN_EINVAL, "output_row_stride < H*V*K");
+  if (output_state_indices && !output_state)
+    return fail(GDN_EINVAL, "output_state_indices needs output_state");
+  if (num_seqs == 0) return ok();
+  if (!q || !k || !v || !o) return fail(GDN_EINVAL, "q, k, v and o must not be NULL");
+  DecodeParams dp{};
+  dp.q = (const u16*)q;
+  dp.k = (const u16*)k;
+  dp.v = (const u16*)v;
+  dp.g = g;
+  dp.beta = beta;
+  dp.o = (u16*)o;
+  dp.num_seqs = num_seqs;
+  dp.H = dims->num_v_heads;
+  dp.Hqk = dims->num_qk_heads;
+  dp.group = dims->num_v_heads / dims->num_qk_heads;
+  dp.scale = eff_scale(dims);
+  dp.mode = 0;
+  dp.rd_idx = initial_state_indices;
+  dp.wr_idx = output_state_indices;
+  dp.idx64 = index_dtype == GDN_INDEX_INT64;
+  dp.init = initial_state;
+  dp.init_stride = initial_row_stride;
+  dp.out = output_state;
+  dp.out_stride = output_row_stride;
+  if (int rc = launched(launch_decode(dp, stream), "decode kernel")) return rc;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Internal definitions shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kDim = 128;    // K = V
+constexpr int kVSlice = 16;  // state rows (v) one recurrence wave owns
+constexpr int kVSlices = kDim / kVSlice;
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Per-sequence rows every prefill kernel consumes (device arrays, [B] int32).
+struct SlotsDev {
+  const int32_t* read;        // initial-state row, -1 = zero state
+  const int32_t* write;       // final-state row, -1 = no store
+  const int32_t* ckpt_start;  // offset of this call's first checkpoint row
+  const int32_t* prefix;      // tokens before the call (chunk alignment)
+  const int32_t* chunk_start; // exclusive scan of chunk counts
+};
+
+// Workspace handed from the intra-chunk kernel to the recurrence kernel.
+// Per (chunk slot c, v-head h):
+//   T fragments  hi/lo  [2][8][64][8] bf16 (16 KiB)   (I + A)^-1
+//   P fragments  hi/lo  [2][8][64][8] bf16 (16 KiB)   decay-masked Q K^T
+//   scalars      [3][64] fp32: beta, gamma = exp(G), dec = exp(G_last - G)
+// Per (chunk slot c, q/k head hq):
+//   K^T fragments [16][64][8] bf16 (16 KiB)
+constexpr int kFragElems = 64 * 8;                 // one 16x16x32 operand, bf16
+constexpr int kTFragsPerMat = 8;                   // 4 row blocks x 2 k-steps
+constexpr int kMatWords = 2 * kTFragsPerMat * kFragElems;   // hi + lo, u16
+constexpr int kKtFrags = 16;                       // 8 row blocks x 2 k-steps
+constexpr int kKtWords = kKtFrags * kFragElems;
+constexpr int kScal = 3 * kChunk;
+
+struct ChunkWs {
+  u16* T;
+  u16* P;
+  float* scal;
+  u16* Kt;
+};
+
+struct ChunkParams {
+  const u16* q;
+  const u16* k;
+  const float* g;
+  const float* beta;
+  const int32_t* cu_seqlens;
+  SlotsDev slots;
+  int num_seqs;
+  int H;
+  int Hqk;
+  int group;  // H / Hqk
+  ChunkWs ws;
+};
+
+struct RecurParams {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  u16* o;
+  const int32_t* cu_seqlens;
+  SlotsDev slots;
+  int num_seqs;
+  int H;
+  int Hqk;
+  int group;
+  float scale;
+  const float* init;
+  int64_t init_stride;
+  float* out;
+  int64_t out_stride;
+  float* ckpt;
+  int64_t ckpt_stride;
+  const void* ckpt_idx;
+  int ckpt_idx64;
+  int ckpt_every;
+  ChunkWs ws;
+};
+
+struct DecodeParams {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  const float* g;
+  const float* beta;
+  u16* o;
+  int num_seqs;
+  int H;
+  int Hqk;
+  int group;
+  float scale;
+  // Rows: mode 0 = explicit index arrays (may be null: row b / the read row),
+  // mode 1 = derived from the page table inside the kernel.
+  int mode;
+  const void* rd_idx;
+  const void* wr_idx;
+  int idx64;
+  const int32_t* page_indices;
+  const int32_t* page_indptr;
+  const int32_t* last_page_len;
+  const float* init;
+  int64_t init_stride;
+  float* out;
+  int64_t out_stride;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_prefill_slots(const int32_t* cu, const int32_t* idx, const int32_t* ptr,
+                                const int32_t* lpl, int B, int page_size, int32_t* read,
+                                int32_t* write, int32_t* ckpt, int32_t* prefix,
+                                int32_t* chunk_start, hipStream_t s);
+hipError_t launch_decode_slots(const int32_t* idx, const int32_t* ptr, const int32_t* lpl,
+                               int B, int32_t* read, int32_t* write, hipStream_t s);
+hipError_t launch_general_slots(const int32_t* cu, int B, const void* sidx, const void* oidx,
+                                const void* cstart, const void* plen, int idx64, int has_init,
+                                int write_final, int32_t* read, int32_t* write, int32_t* ckpt,
+                                int32_t* prefix, int32_t* chunk_start, hipStream_t s);
+hipError_t launch_chunk(const ChunkParams& p, int64_t num_chunk_slots, hipStream_t s);
+hipError_t launch_recur(const RecurParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(uint32_t(b) << 16); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ uint32_t pack2(u16 lo, u16 hi) {
+  return uint32_t(lo) | (uint32_t(hi) << 16);
+}
+
+// Split 8 fp32 values into bf16 hi + lo parts (x ~= hi + lo to ~2^-17).
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = f2bf2(x[2 * i], x[2 * i + 1]);
+    h[i] = w;
+    l[i] = f2bf2(x[2 * i] - __uint_as_float(w << 16), x[2 * i + 1] - __uint_as_float(w & 0xffff0000u));
+  }
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
+// Round 8 fp32 values to bf16 (single part).
+__device__ __forceinline__ bf16x8 round8(const float* x) {
+  u32x4 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = f2bf2(x[2 * i], x[2 * i + 1]);
+  return as_bf16x8(h);
+}
+
+// Row index, within a 64-row operand, of slot j (0..7) of lane group gq (0..3)
+// at k-step ks (0..1 for 64, 0..3 for 128) under the permuted reduction order
+// shared by every operand that comes out of an accumulator: row blocks
+// 2ks and 2ks+1, four consecutive rows at 4*gq.
+__device__ __forceinline__ int perm_row(int ks, int gq, int j) {
+  return 32 * ks + 16 * (j >> 2) + 4 * gq + (j & 3);
+}
+
+#endif
+
+}  // namespace gdn

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every symbol include/*.h declares, and
+rejects host-checkable bad arguments before any launch (CPU only: these calls
+return before touching the HIP runtime)."""
+
+import ctypes as C
+import glob
+import os
+import re
+
+import pytest
+
+from paged_recurrent_state_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[\w\s\*]+?\b(gdn_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.lib_path()):
+        pytest.fail("libgdn_paged.so is not built (run python -m paged_recurrent_state_amd.build)")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"gdn_prefill_paged", "gdn_decode_paged", "gdn_prefill_slots", "gdn_decode_slots",
+            "gdn_prefill", "gdn_decode"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_lib.EXPORTS) == names
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.gdn_version()
+
+
+def dims(H=4, Hqk=2, K=128, V=128, scale=0.0):
+    return _lib.Dims(Hqk, H, K, V, scale)
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    d = dims()
+    a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
+    b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
+    c = lib.gdn_prefill_workspace_size(64 * 100, 10, C.byref(d))
+    assert 0 < a < b < c
+    assert a % 256 == 0 and b % 256 == 0
+    bad = dims(K=64)
+    assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
+
+
+def _prefill_paged(lib, d, page_size=128, stride=4 * 128 * 128, ws=1 << 30, pool=1, cu=1,
+                   B=1, T=64):
+    fake = C.c_void_p(0x1000)  # never dereferenced: the call fails before launching
+    return lib.gdn_prefill_paged(C.byref(d), fake, fake, fake, None, None,
+                                 fake if cu else None, B, T, fake if pool else None, stride,
+                                 fake, fake, fake, page_size, None, fake, fake, ws, None)
+
+
+@pytest.mark.parametrize("ps", [0, -64, 100, 32])
+def test_bad_page_size(lib, ps):
+    assert _prefill_paged(lib, dims(), page_size=ps) == -1
+    assert b"page_size" in lib.gdn_last_error()
+
+
+def test_unsupported_head_dim(lib):
+    assert _prefill_paged(lib, dims(K=64, V=64)) == -2
+    assert _prefill_paged(lib, dims(H=3, Hqk=2)) == -2
+
+
+def test_null_and_stride_errors(lib):
+    assert _prefill_paged(lib, dims(), pool=0) == -1
+    assert _prefill_paged(lib, dims(), cu=0) == -1
+    assert _prefill_paged(lib, dims(), stride=100) == -1
+    assert lib.gdn_prefill_paged(None, None, None, None, None, None, None, 0, 0, None, 0, None,
+                                 None, None, 64, None, None, None, 0, None) == -1
+
+
+def test_workspace_too_small(lib):
+    assert _prefill_paged(lib, dims(), ws=1024) == -4
+    assert b"workspace" in lib.gdn_last_error()
+
+
+def test_general_prefill_companion_rules(lib):
+    d = dims()
+    f = C.c_void_p(0x1000)
+    blk = 4 * 128 * 128
+
+    def call(out_state=f, out_idx=None, final=1, ck_idx=None, ck_starts=f, prefix=f, N=64,
+             ckpt=f, idx_dtype=0):
+        return lib.gdn_prefill(C.byref(d), f, f, f, None, None, f, 1, 64, f, blk, f,
+                               out_state, blk, out_idx, final, ckpt, blk, ck_idx, ck_starts,
+                               prefix, N, idx_dtype, f, f, 1 << 30, None)
+
+    # output_state_indices needs output_state and output_final_state
+    assert call(out_state=None, out_idx=f) == -1
+    assert call(out_idx=f, final=0) == -1
+    # checkpoint rows need N > 0, prefix_lens, checkpoint_cu_starts, state_checkpoints
+    assert call(ck_idx=f, N=0) == -1
+    assert call(ck_idx=f, prefix=None) == -1
+    assert call(ck_idx=f, ck_starts=None) == -1
+    assert call(ck_idx=f, ckpt=None) == -1
+    # N not a multiple of 64 is valid per the page but not built here
+    assert call(ck_idx=f, N=100) == -2
+    assert call(idx_dtype=7) == -1
+
+
+def test_slot_calls_reject_bad_args(lib):
+    f = C.c_void_p(0x1000)
+    out = _lib._PrefillSlotsC(0x1000, 0x1000, 0x1000, 0x1000, None)
+    assert lib.gdn_prefill_slots(f, f, f, f, 2, 64, C.byref(out), None) == -1
+    out = _lib._PrefillSlotsC(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert lib.gdn_prefill_slots(f, f, f, f, 2, 96, C.byref(out), None) == -1
+    assert lib.gdn_prefill_slots(f, f, f, f, -1, 64, C.byref(out), None) == -1
+    dout = _lib._DecodeSlotsC(0x1000, None)
+    assert lib.gdn_decode_slots(f, f, f, 2, C.byref(dout), None) == -1
+
+
+def test_empty_batches_are_no_ops(lib):
+    # num_seqs == 0 returns GDN_OK without launching anything
+    d = dims()
+    assert lib.gdn_prefill_paged(C.byref(d), None, None, None, None, None, C.c_void_p(0x1000),
+                                 0, 0, C.c_void_p(0x1000), 4 * 128 * 128, C.c_void_p(0x1000),
+                                 C.c_void_p(0x1000), C.c_void_p(0x1000), 64, None, None, None,
+                                 0, None) == 0
+    assert lib.gdn_last_error() == b""

@@ -1,0 +1,315 @@
+"""GPU parity on small seeded cases: HIP path vs the fp64 oracle, element by
+element, at sizes that span several chunks and ragged tails, plus the edge
+cases the pages define (empty, zero-length, -1 rows, page boundaries)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import gdn as ogdn
+from oracle import slots as oslots
+from tests.gpu_util import (RowView, changed_rows, check_outputs, check_state, cuda,
+                            pool_rows_cpu)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def lib():
+    import paged_recurrent_state_amd as m
+    m.load()
+    return m
+
+
+def run_prefill_paged(pre, pool, slots=None, scale=None):
+    m = lib()
+    return m.prefill_paged(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"],
+                           pre["cu_seqlens"], pool, pre["page_indices"], pre["page_indptr"],
+                           pre["page_size"], pre["last_page_len"], slots=slots, scale=scale)
+
+
+def oracle_prefill_paged(pre, pool_rows):
+    return ogdn.prefill_paged(pre["q"].cpu(), pre["k"].cpu(), pre["v"].cpu(), pre["g"].cpu(),
+                              pre["beta"].cpu(), pre["cu_seqlens"].cpu(), RowView(pool_rows),
+                              pre["page_indices"].cpu(), pre["page_indptr"].cpu(),
+                              pre["last_page_len"].cpu(), pre["page_size"])
+
+
+def check_paged_prefill(pre, pool):
+    """Run GPU and oracle on the same inputs; check outputs, written states,
+    the write set and every untouched row bit for bit."""
+    rows_in = pool_rows_cpu(pool, [r for r in pre["read_rows"]])
+    before = pool.clone()
+    o = run_prefill_paged(pre, pool)
+    torch.cuda.synchronize()
+    o_ref, writes, _ = oracle_prefill_paged(pre, rows_in)
+    check_outputs(o, o_ref)
+    assert changed_rows(before, pool) == sorted(writes), "page-write set differs"
+    errs = [check_state(pool[r], s, f"row {r}") for r, s in writes.items()]
+    return o, writes, max(errs) if errs else 0.0
+
+
+def test_slot_rows_config0():
+    m = lib()
+    c = cuda(workloads.config0())
+    pre = c["prefill"]
+    sl = m.prefill_slots(pre["cu_seqlens"], pre["page_indices"], pre["page_indptr"],
+                         pre["last_page_len"], 128)
+    ref = oslots.prefill_slots(pre["cu_seqlens"].tolist(), pre["page_indices"].tolist(),
+                               pre["page_indptr"].tolist(), pre["last_page_len"].tolist(), 128)
+    for name in sl._fields:
+        assert getattr(sl, name).tolist() == ref[name], name
+    dec = c["decode"]
+    ds = m.decode_slots(dec["page_indices"], dec["page_indptr"], dec["last_page_len"])
+    dref = oslots.decode_slots(dec["page_indices"].tolist(), dec["page_indptr"].tolist(),
+                               dec["last_page_len"].tolist())
+    for name in ds._fields:
+        assert getattr(ds, name).tolist() == dref[name], name
+
+
+def test_config0_prefill_then_decode():
+    c = cuda(workloads.config0())
+    pool = c["pool"]
+    pre = c["prefill"]
+    o, writes, err = check_paged_prefill(pre, pool)
+    assert sorted(writes) == [4, 5, 9, 11, 14]
+    # page 2 is allocated to seq1 but unlisted: untouched (checked by the set)
+    m = lib()
+    dec = c["decode"]
+    rows_in = pool_rows_cpu(pool, dec["read_rows"])
+    before = pool.clone()
+    od = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
+                        dec["page_indices"], dec["page_indptr"], 128, dec["last_page_len"])
+    torch.cuda.synchronize()
+    od_ref, dwrites, _ = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
+                                           dec["g"].cpu(), dec["beta"].cpu(), RowView(rows_in),
+                                           dec["page_indices"].cpu(), dec["page_indptr"].cpu(),
+                                           dec["last_page_len"].cpu())
+    check_outputs(od, od_ref)
+    assert changed_rows(before, pool) == sorted(dwrites)
+    for r, s in dwrites.items():
+        check_state(pool[r], s)
+
+
+def make_case(prefix, new, ps=64, H=2, Hqk=2, seed=0, g_scale=1.0, num_pages=None):
+    """Paged prefill batch with given prefixes / new lengths; read rows random,
+    all else NaN-poisoned."""
+    gen = workloads.generator(seed)
+    pages = []
+    nxt = 0
+    for p, n in zip(prefix, new):
+        cnt = (p + n + ps - 1) // ps
+        pages.append(list(range(nxt, nxt + cnt)))
+        nxt += cnt
+    num_pages = num_pages or nxt + 1
+    perm = torch.randperm(num_pages, generator=gen).tolist()
+    pages = [[perm[x] for x in pg] for pg in pages]
+    pre = workloads._prefill_batch(prefix, new, pages, ps, Hqk, H, 128, 128, gen, "cpu", g_scale)
+    pool = workloads.nan_pool(num_pages, H, 128, 128)
+    workloads.fill_rows(pool, pre["read_rows"], gen, 1 / math.sqrt(128))
+    return cuda(pre), pool.to(DEV)
+
+
+@pytest.mark.parametrize("prefix,new", [
+    ([0], [1]), ([0], [63]), ([0], [64]), ([0], [65]), ([0], [200]),
+    ([5], [59]), ([5], [60]), ([63], [1]), ([63], [2]), ([64], [64]), ([100], [300]),
+    ([0, 37, 128, 1], [130, 1, 64, 250]),
+])
+def test_prefill_ragged(prefix, new):
+    pre, pool = make_case(prefix, new, seed=sum(prefix) + sum(new))
+    check_paged_prefill(pre, pool)
+
+
+def test_prefill_low_decay_gqa():
+    # slow decay keeps the prefix state alive across chunks; 4 v-heads on 2 q/k heads
+    pre, pool = make_case([70, 0, 300], [400, 333, 129], H=4, Hqk=2, seed=3, g_scale=0.1)
+    check_paged_prefill(pre, pool)
+
+
+def test_prefill_no_decay():
+    pre, pool = make_case([10, 0], [300, 200], seed=4, g_scale=0.0)
+    check_paged_prefill(pre, pool)
+
+
+def test_prefill_zero_length_and_empty():
+    m = lib()
+    # one zero-length sequence among others: it writes nothing
+    pre, pool = make_case([64, 10, 0], [100, 0, 70], seed=5)
+    check_paged_prefill(pre, pool)
+    # a batch whose every sequence has no new tokens leaves the pool unchanged
+    pre, pool = make_case([5, 64], [0, 0], seed=6)
+    before = pool.clone()
+    o = run_prefill_paged(pre, pool)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert changed_rows(before, pool) == []
+
+
+def test_prefill_example_2500_tokens():
+    # pages [7, 3, 12], page 1024, 452 new tokens: reads page 3, writes page 12 only
+    gen = workloads.generator(9)
+    pre = workloads._prefill_batch([2048], [452], [[7, 3, 12]], 1024, 2, 2, 128, 128, gen, "cpu")
+    pool = workloads.nan_pool(16, 2, 128, 128)
+    workloads.fill_rows(pool, [3], gen, 1 / math.sqrt(128))
+    pre, pool = cuda(pre), pool.to(DEV)
+    _, writes, _ = check_paged_prefill(pre, pool)
+    assert sorted(writes) == [12]
+
+
+def test_prefill_slots_passed_equals_derived():
+    m = lib()
+    pre, pool = make_case([0, 37, 128, 1], [130, 1, 64, 250], seed=11)
+    pool2 = pool.clone()
+    o1 = run_prefill_paged(pre, pool)
+    sl = m.prefill_slots(pre["cu_seqlens"], pre["page_indices"], pre["page_indptr"],
+                         pre["last_page_len"], pre["page_size"])
+    o2 = run_prefill_paged(pre, pool2, slots=sl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert changed_rows(pool, pool2) == []
+
+
+def test_decode_paths_agree_and_match_oracle():
+    m = lib()
+    c = cuda(workloads.config2(num_seqs=24, qk_heads=2, v_heads=4, num_pages=24 * 32,
+                               new_page_seqs=8))
+    dec, pool = c["decode"], c["pool"]
+    rows_in = pool_rows_cpu(pool, dec["read_rows"])
+    pool2 = pool.clone()
+    before = pool.clone()
+    o1 = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
+                        dec["page_indices"], dec["page_indptr"], 1024, dec["last_page_len"])
+    sl = m.decode_slots(dec["page_indices"], dec["page_indptr"], dec["last_page_len"])
+    o2 = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool2,
+                        dec["page_indices"], dec["page_indptr"], 1024, dec["last_page_len"],
+                        slots=sl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert changed_rows(pool, pool2) == []
+    o_ref, writes, sref = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
+                                            dec["g"].cpu(), dec["beta"].cpu(), RowView(rows_in),
+                                            dec["page_indices"].cpu(), dec["page_indptr"].cpu(),
+                                            dec["last_page_len"].cpu())
+    assert sl.initial_state_indices.tolist() == sref["initial_state_indices"]
+    assert sl.output_state_indices.tolist() == sref["output_state_indices"]
+    check_outputs(o1, o_ref)
+    assert changed_rows(before, pool) == sorted(writes)
+    for r, s in writes.items():
+        check_state(pool[r], s)
+
+
+@pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
+def test_general_decode_rows(idx_dtype):
+    m = lib()
+    gen = workloads.generator(21)
+    B, H, Hqk = 5, 4, 2
+    t = cuda(workloads.token_inputs(B, Hqk, H, 128, 128, gen))
+    init = (torch.randn(6, H, 128, 128, generator=gen) / math.sqrt(128)).to(DEV)
+    out = workloads.nan_pool(7, H, 128, 128, device=DEV)
+    before = out.clone()
+    rd = torch.tensor([0, -1, 3, 5, 2], dtype=idx_dtype, device=DEV)
+    wr = torch.tensor([1, 2, -1, 6, 0], dtype=idx_dtype, device=DEV)
+    o = m.decode(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=init,
+                 initial_state_indices=rd, output_state=out, output_state_indices=wr)
+    torch.cuda.synchronize()
+    res = ogdn.decode(t["q"].cpu(), t["k"].cpu(), t["v"].cpu(), t["g"].cpu(), t["beta"].cpu(),
+                      initial_state=init.cpu().numpy(), initial_state_indices=rd.tolist(),
+                      output_state_indices=wr.tolist(), shared_pool=False)
+    check_outputs(o, res.o)
+    assert changed_rows(before, out) == sorted(res.final)
+    for r, s in res.final.items():
+        check_state(out[r], s)
+
+
+@pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
+def test_general_prefill_checkpoints(idx_dtype):
+    """Slot-argument prefill in pieces with checkpoints every 128 tokens into a
+    separate buffer (-1 rows skipped) and a padded row stride."""
+    m = lib()
+    H = Hqk = 2
+    N = 128
+    c = workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N, num_rows=3)
+    c = cuda(c)
+    ckpt = workloads.nan_pool(1000 // N, H, 128, 128, device=DEV, row_stride=H * 128 * 128 + 64)
+    slot_pool = c["pool"]
+    ck_rows = c["checkpoint_state_indices"].to(idx_dtype)
+    ref_slot = np.zeros((3, H, 128, 128))
+    ref_ck = {}
+    for call in c["calls"]:
+        cast = {k: call[k].to(idx_dtype) for k in ("state_indices", "output_state_indices",
+                                                   "prefix_lens", "checkpoint_cu_starts")}
+        o = m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"], call["cu_seqlens"],
+                      initial_state=slot_pool, state_indices=cast["state_indices"],
+                      output_state=slot_pool, output_state_indices=cast["output_state_indices"],
+                      output_final_state=True, state_checkpoints=ckpt,
+                      checkpoint_state_indices=ck_rows,
+                      checkpoint_cu_starts=cast["checkpoint_cu_starts"],
+                      prefix_lens=cast["prefix_lens"], checkpoint_every_n_tokens=N)
+        torch.cuda.synchronize()
+        res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(), call["g"].cpu(),
+                           call["beta"].cpu(), call["cu_seqlens"].cpu(), initial_state=ref_slot,
+                           state_indices=call["state_indices"].tolist(),
+                           output_final_state=True,
+                           output_state_indices=call["output_state_indices"].tolist(),
+                           checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
+                           checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
+                           prefix_lens=call["prefix_lens"].tolist(), checkpoint_every_n_tokens=N,
+                           shared_pool=False)
+        check_outputs(o, res.o)
+        ref_slot = ogdn.apply_writes(ref_slot, res.final)
+        ref_ck.update(res.checkpoints)
+        check_state(slot_pool[c["slot"]], ref_slot[c["slot"]], "slot")
+    n_ck = 1000 // N
+    got = [r for r in range(n_ck) if torch.isfinite(ckpt[r]).all()]
+    assert got == sorted(ref_ck) == [r for r in range(n_ck) if r % 2 == 0]
+    for r, s in ref_ck.items():
+        check_state(ckpt[r], s, f"checkpoint {r}")
+    # odd rows kept their NaN bits
+    for r in range(n_ck):
+        if r % 2:
+            assert (ckpt[r].view(torch.int32) == workloads.NAN_BITS).all()
+
+
+def test_general_prefill_no_state_buffers():
+    """No initial state, no final store: outputs only, from the zero state."""
+    m = lib()
+    gen = workloads.generator(31)
+    t = cuda(workloads.token_inputs(300, 2, 2, 128, 128, gen))
+    cu = torch.tensor([0, 100, 100, 300], dtype=torch.int32, device=DEV)
+    o = m.prefill(t["q"], t["k"], t["v"], None, None, cu)
+    torch.cuda.synchronize()
+    res = ogdn.prefill(t["q"].cpu(), t["k"].cpu(), t["v"].cpu(), None, None, cu.cpu())
+    check_outputs(o, res.o)
+
+
+def test_split_invariance_on_gpu():
+    """Prefill at any split resumes from the written page: GPU split run vs the
+    oracle's unsplit run, within tolerance."""
+    m = lib()
+    ps = 128
+    T = 700
+    gen = workloads.generator(41)
+    t = cuda(workloads.token_inputs(T, 2, 2, 128, 128, gen, g_scale=0.1))
+    pages = [9, 2, 7, 4, 0, 6]
+    pool = workloads.nan_pool(10, 2, 128, 128, device=DEV)
+    o_ref = ogdn.prefill_paged(t["q"].cpu(), t["k"].cpu(), t["v"].cpu(), t["g"].cpu(),
+                               t["beta"].cpu(), [0, T], np.zeros((10, 2, 128, 128)),
+                               pages, [0, 6], [T - 5 * ps], ps)
+    outs = []
+    cuts = [0, 77, 128, 129, 450, T]
+    for a, b in zip(cuts, cuts[1:]):
+        n = (b + ps - 1) // ps
+        idx = torch.tensor(pages[:n], dtype=torch.int32, device=DEV)
+        ptr = torch.tensor([0, n], dtype=torch.int32, device=DEV)
+        lpl = torch.tensor([b - (n - 1) * ps], dtype=torch.int32, device=DEV)
+        cu = torch.tensor([0, b - a], dtype=torch.int32, device=DEV)
+        outs.append(m.prefill_paged(t["q"][a:b].contiguous(), t["k"][a:b].contiguous(),
+                                    t["v"][a:b].contiguous(), t["g"][a:b].contiguous(),
+                                    t["beta"][a:b].contiguous(), cu, pool, idx, ptr, ps, lpl))
+    torch.cuda.synchronize()
+    check_outputs(torch.cat(outs), o_ref[0])
+    for r, s in o_ref[1].items():
+        check_state(pool[r], s, f"page {r}")
