@@ -38,28 +38,16 @@ int launched(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace: the per-sequence rows (5 x [B] int32) and the launch order ([B]).
 struct WsLayout {
-  int64_t nc;  // chunk slots: >= sum over sequences of ceil(((p mod 64) + L) / 64)
-  size_t slots, T, P, scal, Kt, total;
+  size_t slots, order, total;
 };
 
-WsLayout ws_layout(int64_t T, int B, int H, int Hqk) {
+WsLayout ws_layout(int64_t /*T*/, int B) {
   WsLayout w;
-  // ceil((r + L) / 64) with r < 64 is at most (L + 126) / 64, so the chunks of
-  // a batch never exceed T / 64 + 2 B.
-  w.nc = T / kChunk + 2 * (int64_t)B + 1;
-  size_t off = 0;
-  w.slots = off;
-  off += align256((size_t)5 * B * sizeof(int32_t));
-  w.T = off;
-  off += align256((size_t)w.nc * H * kMatWords * sizeof(u16));
-  w.P = off;
-  off += align256((size_t)w.nc * H * kMatWords * sizeof(u16));
-  w.scal = off;
-  off += align256((size_t)w.nc * H * kScal * sizeof(float));
-  w.Kt = off;
-  off += align256((size_t)w.nc * Hqk * kKtWords * sizeof(u16));
-  w.total = off;
+  w.slots = 0;
+  w.order = align256((size_t)5 * B * sizeof(int32_t));
+  w.total = w.order + align256((size_t)B * sizeof(int32_t));
   return w;
 }
 
@@ -101,57 +89,38 @@ SlotsDev carve_slots(void* ws, const WsLayout& L, int B) {
   return SlotsDev{base, base + B, base + 2 * B, base + 3 * B, base + 4 * B};
 }
 
-ChunkWs carve_chunk(void* ws, const WsLayout& L) {
-  char* w = (char*)ws;
-  return ChunkWs{(u16*)(w + L.T), (u16*)(w + L.P), (float*)(w + L.scal), (u16*)(w + L.Kt)};
-}
-
-// Launch the intra-chunk and recurrence kernels once the rows are on the device.
+// Launch the fused prefill once the rows are on the device.
 int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const int32_t* cu, int B,
                 const SlotsDev& sd, const WsLayout& L, void* ws, const float* init,
                 int64_t init_stride, float* out, int64_t out_stride, float* ckpt,
                 int64_t ckpt_stride, const void* ckpt_idx, int ckpt_idx64, int ckpt_every,
                 void* o, hipStream_t stream) {
-  ChunkParams cp;
-  cp.q = (const u16*)q;
-  cp.k = (const u16*)k;
-  cp.g = g;
-  cp.beta = beta;
-  cp.cu_seqlens = cu;
-  cp.slots = sd;
-  cp.num_seqs = B;
-  cp.H = d->num_v_heads;
-  cp.Hqk = d->num_qk_heads;
-  cp.group = d->num_v_heads / d->num_qk_heads;
-  cp.ws = carve_chunk(ws, L);
-  int rc = launched(launch_chunk(cp, L.nc, stream), "intra-chunk kernel");
-  if (rc) return rc;
-
-  RecurParams rp;
-  rp.q = (const u16*)q;
-  rp.k = (const u16*)k;
-  rp.v = (const u16*)v;
-  rp.o = (u16*)o;
-  rp.cu_seqlens = cu;
-  rp.slots = sd;
-  rp.num_seqs = B;
-  rp.H = d->num_v_heads;
-  rp.Hqk = d->num_qk_heads;
-  rp.group = d->num_v_heads / d->num_qk_heads;
-  rp.scale = eff_scale(d);
-  rp.init = init;
-  rp.init_stride = init_stride;
-  rp.out = out;
-  rp.out_stride = out_stride;
-  rp.ckpt = ckpt;
-  rp.ckpt_stride = ckpt_stride;
-  rp.ckpt_idx = ckpt_idx;
-  rp.ckpt_idx64 = ckpt_idx64;
-  rp.ckpt_every = ckpt_every;
-  rp.ws = cp.ws;
-  rc = launched(launch_recur(rp, stream), "recurrence kernel");
-  if (rc) return rc;
+  PrefillParams pp;
+  pp.q = (const u16*)q;
+  pp.k = (const u16*)k;
+  pp.v = (const u16*)v;
+  pp.g = g;
+  pp.beta = beta;
+  pp.o = (u16*)o;
+  pp.cu_seqlens = cu;
+  pp.slots = sd;
+  pp.order = (int32_t*)((char*)ws + L.order);
+  pp.num_seqs = B;
+  pp.H = d->num_v_heads;
+  pp.Hqk = d->num_qk_heads;
+  pp.group = d->num_v_heads / d->num_qk_heads;
+  pp.scale = eff_scale(d);
+  pp.init = init;
+  pp.init_stride = init_stride;
+  pp.out = out;
+  pp.out_stride = out_stride;
+  pp.ckpt = ckpt;
+  pp.ckpt_stride = ckpt_stride;
+  pp.ckpt_idx = ckpt_idx;
+  pp.ckpt_idx64 = ckpt_idx64;
+  pp.ckpt_every = ckpt_every;
+  if (int rc = launched(launch_prefill(pp, stream), "prefill kernel")) return rc;
   return ok();
 }
 
@@ -165,7 +134,7 @@ const char* gdn_version(void) { return "gdn_paged 0.1.0 (gfx950)"; }
 
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, const gdn_dims_t* dims) {
   if (check_dims(dims) != GDN_OK || total_tokens < 0 || num_seqs < 0) return 0;
-  return ws_layout(total_tokens, num_seqs, dims->num_v_heads, dims->num_qk_heads).total;
+  return ws_layout(total_tokens, num_seqs).total;
 }
 
 int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,
@@ -225,7 +194,7 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
   if (num_seqs == 0) return ok();
   if (total_tokens > 0)
     if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, dims->num_qk_heads);
+  const WsLayout L = ws_layout(total_tokens, num_seqs);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
@@ -342,7 +311,7 @@ int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void
   }
   if (num_seqs == 0 || total_tokens == 0) return ok();
   if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, dims->num_qk_heads);
+  const WsLayout L = ws_layout(total_tokens, num_seqs);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);

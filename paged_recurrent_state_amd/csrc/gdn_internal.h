@@ -8,8 +8,6 @@ namespace gdn {
 
 constexpr int kChunk = 64;   // tokens per chunk
 constexpr int kDim = 128;    // K = V
-constexpr int kVSlice = 16;  // state rows (v) one recurrence wave owns
-constexpr int kVSlices = kDim / kVSlice;
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -26,52 +24,22 @@ struct SlotsDev {
   const int32_t* chunk_start; // exclusive scan of chunk counts
 };
 
-// Workspace handed from the intra-chunk kernel to the recurrence kernel.
-// Per (chunk slot c, v-head h):
-//   T fragments  hi/lo  [2][8][64][8] bf16 (16 KiB)   (I + A)^-1
-//   P fragments  hi/lo  [2][8][64][8] bf16 (16 KiB)   decay-masked Q K^T
-//   scalars      [3][64] fp32: beta, gamma = exp(G), dec = exp(G_last - G)
-// Per (chunk slot c, q/k head hq):
-//   K^T fragments [16][64][8] bf16 (16 KiB)
-constexpr int kFragElems = 64 * 8;                 // one 16x16x32 operand, bf16
-constexpr int kTFragsPerMat = 8;                   // 4 row blocks x 2 k-steps
-constexpr int kMatWords = 2 * kTFragsPerMat * kFragElems;   // hi + lo, u16
-constexpr int kKtFrags = 16;                       // 8 row blocks x 2 k-steps
-constexpr int kKtWords = kKtFrags * kFragElems;
-constexpr int kScal = 3 * kChunk;
+constexpr int kFragElems = 64 * 8;  // one 16x16x32 MFMA operand fragment, bf16 elements
 
-struct ChunkWs {
-  u16* T;
-  u16* P;
-  float* scal;
-  u16* Kt;
-};
-
-struct ChunkParams {
+struct PrefillParams {
   const u16* q;
   const u16* k;
+  const u16* v;
   const float* g;
   const float* beta;
+  u16* o;
   const int32_t* cu_seqlens;
   SlotsDev slots;
+  int32_t* order;  // [B] workspace: sequences longest first
   int num_seqs;
   int H;
   int Hqk;
   int group;  // H / Hqk
-  ChunkWs ws;
-};
-
-struct RecurParams {
-  const u16* q;
-  const u16* k;
-  const u16* v;
-  u16* o;
-  const int32_t* cu_seqlens;
-  SlotsDev slots;
-  int num_seqs;
-  int H;
-  int Hqk;
-  int group;
   float scale;
   const float* init;
   int64_t init_stride;
@@ -82,7 +50,6 @@ struct RecurParams {
   const void* ckpt_idx;
   int ckpt_idx64;
   int ckpt_every;
-  ChunkWs ws;
 };
 
 struct DecodeParams {
@@ -123,8 +90,8 @@ hipError_t launch_general_slots(const int32_t* cu, int B, const void* sidx, cons
                                 const void* cstart, const void* plen, int idx64, int has_init,
                                 int write_final, int32_t* read, int32_t* write, int32_t* ckpt,
                                 int32_t* prefix, int32_t* chunk_start, hipStream_t s);
-hipError_t launch_chunk(const ChunkParams& p, int64_t num_chunk_slots, hipStream_t s);
-hipError_t launch_recur(const RecurParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+size_t prefill_lds_bytes();
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers

@@ -48,13 +48,14 @@ def dims(H=4, Hqk=2, K=128, V=128, scale=0.0):
     return _lib.Dims(Hqk, H, K, V, scale)
 
 
-def test_workspace_size_grows_with_tokens(lib):
+def test_workspace_size(lib):
     d = dims()
     a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
     b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
-    c = lib.gdn_prefill_workspace_size(64 * 100, 10, C.byref(d))
-    assert 0 < a < b < c
-    assert a % 256 == 0 and b % 256 == 0
+    c = lib.gdn_prefill_workspace_size(64 * 100, 300, C.byref(d))
+    # per-sequence rows and the launch order only: independent of the token count
+    assert 0 < a == b < c
+    assert a % 256 == 0 and c % 256 == 0
     bad = dims(K=64)
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
 
@@ -87,7 +88,7 @@ def test_null_and_stride_errors(lib):
 
 
 def test_workspace_too_small(lib):
-    assert _prefill_paged(lib, dims(), ws=1024) == -4
+    assert _prefill_paged(lib, dims(), ws=16) == -4
     assert b"workspace" in lib.gdn_last_error()
 
 
