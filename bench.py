@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (reference for "
+                         "hardware byte counters); reported as copy_GBps")
     return ap.parse_args()
 
 
@@ -182,7 +185,7 @@ def hybrid(args, torch, gdn, workloads):
                 "traffic": None, "per_launch_bytes": dc_bytes, "avg_launch_ms": t_dc_ms}
     else:
         ach = pf_bytes / (t_pf_ms / 1e3) / 1e9
-        roof = {"kernel": "prefill (chunk_kernel + recur_kernel)", "bound": "hbm",
+        roof = {"kernel": "prefill_kernel", "bound": "hbm",
                 "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBPS, "traffic": None, "per_launch_bytes": pf_bytes,
                 "avg_launch_ms": t_pf_ms}
@@ -323,6 +326,22 @@ def main():
 
     gdn.load()
     torch.manual_seed(0)
+    copy_gbps = None
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        reps = 5
+        for _ in range(reps):
+            dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * n * reps / (a.elapsed_time(b) / 1e3) / 1e9
+        del src, dst
     if args.workload == "hybrid":
         line, cpu_inputs, pool = hybrid(args, torch, gdn, workloads)
     else:
@@ -335,6 +354,8 @@ def main():
         pool_rows = {int(r): pool[int(r)].cpu().numpy() for r in rows if int(r) >= 0}
         line["cpu_baseline"] = cpu_baseline(pcpu, dcpu, pool_rows, args.cpu_sample_tokens,
                                             args.layers, T, ndec)
+    if copy_gbps is not None:
+        line["copy_GBps"] = copy_gbps
     print(json.dumps(line), flush=True)
 
 
