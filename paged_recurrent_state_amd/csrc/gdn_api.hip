@@ -38,16 +38,28 @@ int launched(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: the per-sequence rows (5 x [B] int32) and the launch order ([B]).
+// Workspace: the per-sequence rows (5 x [B] int32), the launch order ([B]) and,
+// per (chunk slot, v-head), the intra-chunk record (T fragments + scalars).
+// A sequence with L new tokens spans ceil(((prefix mod 64) + L) / 64) <=
+// (L + 126) / 64 chunks, so a batch never has more than T / 64 + 2 B of them.
 struct WsLayout {
-  size_t slots, order, total;
+  int64_t nc;
+  size_t slots, order, T, scal, total;
 };
 
-WsLayout ws_layout(int64_t /*T*/, int B) {
+WsLayout ws_layout(int64_t T, int B, int H) {
   WsLayout w;
-  w.slots = 0;
-  w.order = align256((size_t)5 * B * sizeof(int32_t));
-  w.total = w.order + align256((size_t)B * sizeof(int32_t));
+  w.nc = T / kChunk + 2 * (int64_t)B + 1;
+  size_t off = 0;
+  w.slots = off;
+  off += align256((size_t)5 * B * sizeof(int32_t));
+  w.order = off;
+  off += align256((size_t)B * sizeof(int32_t));
+  w.T = off;
+  off += align256((size_t)w.nc * H * kRecWords * sizeof(u16));
+  w.scal = off;
+  off += align256((size_t)w.nc * H * kRecScal * sizeof(float));
+  w.total = off;
   return w;
 }
 
@@ -106,6 +118,8 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.cu_seqlens = cu;
   pp.slots = sd;
   pp.order = (int32_t*)((char*)ws + L.order);
+  pp.ws_T = (u16*)((char*)ws + L.T);
+  pp.ws_scal = (float*)((char*)ws + L.scal);
   pp.num_seqs = B;
   pp.H = d->num_v_heads;
   pp.Hqk = d->num_qk_heads;
@@ -120,7 +134,7 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.ckpt_idx = ckpt_idx;
   pp.ckpt_idx64 = ckpt_idx64;
   pp.ckpt_every = ckpt_every;
-  if (int rc = launched(launch_prefill(pp, stream), "prefill kernel")) return rc;
+  if (int rc = launched(launch_prefill(pp, L.nc, stream), "prefill kernels")) return rc;
   return ok();
 }
 
@@ -134,7 +148,7 @@ const char* gdn_version(void) { return "gdn_paged 0.1.0 (gfx950)"; }
 
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, const gdn_dims_t* dims) {
   if (check_dims(dims) != GDN_OK || total_tokens < 0 || num_seqs < 0) return 0;
-  return ws_layout(total_tokens, num_seqs).total;
+  return ws_layout(total_tokens, num_seqs, dims->num_v_heads).total;
 }
 
 int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,
@@ -194,7 +208,7 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
   if (num_seqs == 0) return ok();
   if (total_tokens > 0)
     if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs);
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
@@ -311,7 +325,7 @@ int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void
   }
   if (num_seqs == 0 || total_tokens == 0) return ok();
   if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs);
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);

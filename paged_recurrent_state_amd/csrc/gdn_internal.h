@@ -26,6 +26,12 @@ struct SlotsDev {
 
 constexpr int kFragElems = 64 * 8;  // one 16x16x32 MFMA operand fragment, bf16 elements
 
+// Per (chunk slot, v-head) record the intra-chunk kernel hands to the
+// recurrence: T = (I + A)^-1 as 8 hi + 8 lo bf16 operand fragments, and the
+// per-row scalars beta, G (log2 units), gamma = 2^G, exp(G_last - G).
+constexpr int kRecWords = 2 * 8 * kFragElems;  // bf16 elements (16 KiB)
+constexpr int kRecScal = 4 * kChunk;           // floats (1 KiB)
+
 struct PrefillParams {
   const u16* q;
   const u16* k;
@@ -36,6 +42,8 @@ struct PrefillParams {
   const int32_t* cu_seqlens;
   SlotsDev slots;
   int32_t* order;  // [B] workspace: sequences longest first
+  u16* ws_T;       // [chunk slots][H][kRecWords]
+  float* ws_scal;  // [chunk slots][H][kRecScal]
   int num_seqs;
   int H;
   int Hqk;
@@ -90,8 +98,7 @@ hipError_t launch_general_slots(const int32_t* cu, int B, const void* sidx, cons
                                 const void* cstart, const void* plen, int idx64, int has_init,
                                 int write_final, int32_t* read, int32_t* write, int32_t* ckpt,
                                 int32_t* prefix, int32_t* chunk_start, hipStream_t s);
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
-size_t prefill_lds_bytes();
+hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- device helpers

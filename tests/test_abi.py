@@ -53,9 +53,11 @@ def test_workspace_size(lib):
     a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
     b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
     c = lib.gdn_prefill_workspace_size(64 * 100, 300, C.byref(d))
-    # per-sequence rows and the launch order only: independent of the token count
-    assert 0 < a == b < c
-    assert a % 256 == 0 and c % 256 == 0
+    # rows + launch order per sequence, and one 17 KiB intra-chunk record per
+    # (chunk slot, v-head) with at most T/64 + 2B + 1 chunk slots
+    assert 0 < a < b < c
+    assert a % 256 == 0 and b % 256 == 0
+    assert b - a == 100 * 4 * (16384 + 1024)
     bad = dims(K=64)
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
 
@@ -88,7 +90,7 @@ def test_null_and_stride_errors(lib):
 
 
 def test_workspace_too_small(lib):
-    assert _prefill_paged(lib, dims(), ws=16) == -4
+    assert _prefill_paged(lib, dims(), ws=1024) == -4
     assert b"workspace" in lib.gdn_last_error()
 
 

@@ -75,6 +75,7 @@ def test_config0_prefill_then_decode():
     pool = c["pool"]
     pre = c["prefill"]
     o, writes, err = check_paged_prefill(pre, pool)
+    print(f"config0 prefill: worst state rel {err:.2e}")
     assert sorted(writes) == [4, 5, 9, 11, 14]
     # page 2 is allocated to seq1 but unlisted: untouched (checked by the set)
     m = lib()
@@ -126,12 +127,14 @@ def test_prefill_ragged(prefix, new):
 def test_prefill_low_decay_gqa():
     # slow decay keeps the prefix state alive across chunks; 4 v-heads on 2 q/k heads
     pre, pool = make_case([70, 0, 300], [400, 333, 129], H=4, Hqk=2, seed=3, g_scale=0.1)
-    check_paged_prefill(pre, pool)
+    _, _, err = check_paged_prefill(pre, pool)
+    print(f"low decay: worst state rel {err:.2e}")
 
 
 def test_prefill_no_decay():
     pre, pool = make_case([10, 0], [300, 200], seed=4, g_scale=0.0)
-    check_paged_prefill(pre, pool)
+    _, _, err = check_paged_prefill(pre, pool)
+    print(f"no decay: worst state rel {err:.2e}")
 
 
 def test_prefill_zero_length_and_empty():
