@@ -56,11 +56,6 @@ __device__ __forceinline__ int64_t ld_index(const void* p, int i, int idx64) {
   return idx64 ? ((const int64_t*)p)[i] : (int64_t)((const int32_t*)p)[i];
 }
 
-__device__ __forceinline__ void store_state(float* dst, const f32x4 (&accS)[8]) {
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) *(f32x4*)(dst + 16 * mb) = accS[mb];
-}
-
 __device__ __forceinline__ void split_rows(const f32x4 (&x)[4], int ks, bf16x8& hi, bf16x8& lo) {
   float v[8];
 #pragma unroll
@@ -305,21 +300,38 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
+// rec_kernel keeps its 64x128 tiles in plain fragment order: fragment
+// (t/16, k/32), lane (t%16) + 16*((k%32)/8), slot k%8 -- every 16-byte unit
+// is 8 consecutive k of one row, as it sits in memory.  The state's k index
+// is relabelled to match: accumulator block mb, lane group gq, row r holds
+// k = 32*(mb/2) + 8*gq + 4*(mb%2) + r, so blocks 2ks and 2ks+1 of a lane are
+// exactly the 8 consecutive k its B operand needs for k-step ks.
+constexpr int kOsPitch = kDim + 8;  // bf16 row pitch of the output tile
+
 struct RecSmem {
-  u16 Kf[kTileWords];     // K tile: [row block][k-step][lane][8]
-  u16 Qf[kTileWords];     // Q tile, same order
+  u16 Kf[kTileWords];     // K tile, plain fragment order
+  u16 Qf[kTileWords];     // Q tile
+  u16 Vf[kTileWords];     // V tile
   u16 Ktf[kKtWordsL];     // K^T fragments: [k block][t-step][lane][8]
   u16 Tf[2 * kMatFrag];   // T fragments, hi then lo (from wy_kernel)
   u16 Pf[2 * kMatFrag];   // P fragments, hi then lo
-  u16 Vs[kWaves][64][16]; // v tile: wave w's columns, lane's rows 16*mt + 4*gq + r
-  u16 Os[kChunk][kDim];   // output tile, written to memory after the chunk
+  u16 Os[kChunk][kOsPitch];  // output tile, written to memory after the chunk
   float scal[4][kChunk];  // beta, G, gamma, exp(G_last - G)
 };
 
+// k of accumulator row (block mb, lane group gq, r = 0)
+__device__ __forceinline__ int state_k(int mb, int gq) { return 32 * (mb >> 1) + 8 * gq + 4 * (mb & 1); }
+
+// dst points at the lane's state row (v), k = 0
+__device__ __forceinline__ void store_state(float* dst, const f32x4 (&accS)[8], int gq) {
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) *(f32x4*)(dst + state_k(mb, gq)) = accS[mb];
+}
+
 // Next chunk's inputs, held in registers while the current chunk computes.
 struct Prefetch {
-  u32x4 kq[4];  // two 16-byte pieces of the K tile, two of the Q tile
-  u32x4 v[2];   // two 16-byte pieces of the v tile
+  u32x4 kq[4];  // two 16-byte units of the K tile, two of the Q tile
+  u32x4 v[2];   // two 16-byte units of the V tile
   u32x4 tf[2];  // two 16-byte pieces of the T fragments
   float sc;     // one scalar
 };
@@ -328,15 +340,19 @@ struct Seq {
   int tok0, L, hq, h;
 };
 
-// Issue the loads of chunk slot c whose row 0 is new token n0.  Rows outside
-// the sequence read token 0 of the sequence (always in bounds); their values
-// are replaced by zeros where they are consumed, so nothing here waits.
+// Issue the loads of chunk slot c whose row 0 is new token n0.  Wave w, item
+// i fetches tile fragment 2w + i; its lane l takes row 16*(fragment/4) + l%16
+// and k-group 4*(fragment%4) + l/16 (16 rows x 64 contiguous bytes per
+// instruction).  Rows outside the sequence read token 0 of the sequence
+// (always in bounds); their values become zeros when stored to LDS, so
+// nothing here waits.
 __device__ __forceinline__ void load_chunk(Prefetch& pf, const PrefillParams& p, const Seq& s,
                                            int64_t c, int n0, int tid) {
+  const int lane = tid & 63, wid = tid >> 6;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int it = tid + kThreads * i;
-    const int row = it >> 4, seg = it & 15;
+    const int f = 2 * wid + i;
+    const int row = 16 * (f >> 2) + (lane & 15), seg = 4 * (f & 3) + (lane >> 4);
     const int n = n0 + row;
     const bool valid = (unsigned)n < (unsigned)s.L;
     const int64_t tok = (int64_t)s.tok0 + (valid ? n : 0);
@@ -355,28 +371,16 @@ __device__ __forceinline__ void load_chunk(Prefetch& pf, const PrefillParams& p,
 __device__ __forceinline__ void store_chunk(const Prefetch& pf, RecSmem& sm, const Seq& s, int n0,
                                             int tid) {
   const u32x4 z = {0u, 0u, 0u, 0u};
+  const int lane = tid & 63, wid = tid >> 6;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int it = tid + kThreads * i;
-    const int row = it >> 4, seg = it & 15, k0 = seg * 8;
+    const int f = 2 * wid + i;
+    const int row = 16 * (f >> 2) + (lane & 15);
     const bool valid = (unsigned)(n0 + row) < (unsigned)s.L;
-    const u32x4 kv = valid ? pf.kq[i] : z;
-    const u32x4 qv = valid ? pf.kq[2 + i] : z;
-    const u32x4 vv = valid ? pf.v[i] : z;
-    *(u32x2*)&sm.Kf[tile_off(row, k0)] = u32x2{kv.x, kv.y};
-    *(u32x2*)&sm.Kf[tile_off(row, k0 + 4)] = u32x2{kv.z, kv.w};
-    *(u32x2*)&sm.Qf[tile_off(row, k0)] = u32x2{qv.x, qv.y};
-    *(u32x2*)&sm.Qf[tile_off(row, k0 + 4)] = u32x2{qv.z, qv.w};
-    // v: columns seg*8 .. seg*8+7 of token row `row` go to wave seg/2, lanes
-    // 8*(seg&1) + c + 16*gq, slot 4*mt + r (row = 16*mt + 4*gq + r)
-    const int w = seg >> 1;
-    const int lbase = 8 * (seg & 1) + 16 * ((row & 15) >> 2);
-    const int slot = 4 * (row >> 4) + (row & 3);
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const uint32_t word = vv[cc >> 1];
-      sm.Vs[w][lbase + cc][slot] = u16((cc & 1) ? (word >> 16) : (word & 0xffffu));
-    }
+    const int at = (f * 64 + lane) * 8;  // consecutive lanes, consecutive 16 bytes
+    *(u32x4*)&sm.Kf[at] = valid ? pf.kq[i] : z;
+    *(u32x4*)&sm.Qf[at] = valid ? pf.kq[2 + i] : z;
+    *(u32x4*)&sm.Vf[at] = valid ? pf.v[i] : z;
     *(u32x4*)&sm.Tf[(tid + kThreads * i) * 8] = pf.tf[i];
   }
   if (tid < kRecScal) (&sm.scal[0][0])[tid] = pf.sc;
@@ -390,7 +394,7 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
     const int it = tid + kThreads * i;
     const int row = it >> 4, seg = it & 15;
     const int nn = n0 + row;
-    const u32x4 w = *(const u32x4*)&sm.Os[row][seg * 8];
+    const u32x4 w = *(const u32x4*)&sm.Os[row][seg * 8];  // pitch keeps 16-byte alignment
     if ((unsigned)nn < (unsigned)s.L)
       *(u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + seg * 8) = w;
   }
@@ -418,17 +422,23 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   const int rd = p.slots.read[b];
   const int wr = p.slots.write[b];
   const int vrow = 16 * wid + n16;
-  const int64_t head_off = ((int64_t)s.h * kDim + vrow) * kDim + 4 * gq;
+  const int64_t head_off = ((int64_t)s.h * kDim + vrow) * kDim;
 
   f32x4 accS[8];
   if (rd >= 0 && p.init) {
     const float* src = p.init + (int64_t)rd * p.init_stride + head_off;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) accS[mb] = *(const f32x4*)(src + 16 * mb);
+    for (int mb = 0; mb < 8; ++mb) accS[mb] = *(const f32x4*)(src + state_k(mb, gq));
   } else {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) accS[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+
+  // 0/1 operand that picks this wave's 16 v columns out of a V fragment:
+  // B[8*gq + j][n] = 1 where 8*gq + j == 16*(wid%2) + n
+  bf16x8 vsel;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vsel[j] = 8 * gq + j == 16 * (wid & 1) + n16 ? (__bf16)1.0f : (__bf16)0.0f;
 
   const int nbase = (pre & ~(kChunk - 1)) - pre;  // new-token index of chunk 0's row 0
   Prefetch pf;
@@ -476,14 +486,15 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{hw[0], hw[1]};
       *(u32x2*)&sm.Pf[kMatFrag + (f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{lw[0], lw[1]};
     }
-    // K^T fragments: K[t][k] gathered from the fragment-ordered K tile
+    // K^T fragments: K[t][k] gathered from the K tile (rows k in the state's order)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int it = tid + kThreads * i;
       const int frag = it >> 6, ln = it & 63;
       const int mk = frag >> 1, ks = frag & 1;
-      const int kcol = 16 * mk + (ln & 15), g4 = ln >> 4;
-      const int kin = tile_off(0, kcol & ~3) + (kcol & 3);  // offset of (row 0, kcol)
+      const int kcol = state_k(mk, (ln & 15) >> 2) + (ln & 3), g4 = ln >> 4;
+      // offset of (row 0, kcol) in the plain fragment order
+      const int kin = ((kcol >> 5) * 64 + 16 * ((kcol & 31) >> 3)) * 8 + (kcol & 7);
       u16 e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -505,11 +516,10 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       split8(v, Shi[ks], Slo[ks]);
     }
 
-    // Y = K S^T, then R = beta (V - gamma Y)
+    // Y = K S^T, then R = beta (V - gamma Y); V's 16 columns enter through
+    // the selection operand (exact: one product by 1 per element)
     f32x4 R[4];
     {
-      const u32x4 va = *(const u32x4*)&sm.Vs[wid][lane][0];
-      const u32x4 vb = *(const u32x4*)&sm.Vs[wid][lane][8];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
@@ -521,12 +531,12 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
         }
         const f32x4 bt = *(const f32x4*)&sm.scal[0][16 * mt + 4 * gq];
         const f32x4 gm = *(const f32x4*)&sm.scal[2][16 * mt + 4 * gq];
-        const uint32_t w0 = mt < 2 ? va[2 * mt] : vb[2 * mt - 4];
-        const uint32_t w1 = mt < 2 ? va[2 * mt + 1] : vb[2 * mt - 3];
-        const float vx[4] = {__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u),
-                             __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xffff0000u)};
+        f32x4 c;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[mt][r] = bt[r] * (vx[r] - gm[r] * y[r]);
+        for (int r = 0; r < 4; ++r) c[r] = -gm[r] * y[r];
+        c = mfma16x16x32(lds_frag(sm.Vf, mt * 4 + (wid >> 1), lane), vsel, c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[mt][r] = bt[r] * c[r];
       }
     }
 
@@ -551,31 +561,33 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       }
     }
 
-    // O = scale (gamma Q S^T + P E), stored per row block
+    // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
+    // state fragments and E act as A operands, Q and P fragments as B, so a
+    // lane ends up with 4 adjacent v of one token (one 8-byte LDS store)
     {
       bf16x8 Ehi[2], Elo[2];
       split_rows(E, 0, Ehi[0], Elo[0]);
       split_rows(E, 1, Ehi[1], Elo[1]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        // output-only products: Q S^T with the state's hi part, P E without
-        // the P_lo E_lo-sized term (the bf16 output rounding dominates both)
+        // output-only products: S Q^T with the state's hi part, E^T P^T
+        // without the E_lo P_lo-sized term (the bf16 output rounding
+        // dominates both)
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) z = mfma16x16x32(lds_frag(sm.Qf, mt * 4 + ks, lane), Shi[ks], z);
-        const f32x4 gm = *(const f32x4*)&sm.scal[2][16 * mt + 4 * gq];
+        for (int ks = 0; ks < 4; ++ks) z = mfma16x16x32(Shi[ks], lds_frag(sm.Qf, mt * 4 + ks, lane), z);
+        const float gm = sm.scal[2][16 * mt + n16];
         f32x4 O;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[r] = gm[r] * z[r];
+        for (int r = 0; r < 4; ++r) O[r] = gm * z[r];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int f = mt * 2 + ks;
-          const bf16x8 ph = lds_frag(sm.Pf, f, lane);
-          O = mfma16x16x32(ph, Ehi[ks], O);
-          O = mfma16x16x32(ph, Elo[ks], O);
+          const bf16x8 ph = lds_frag(sm.Pf, mt * 2 + ks, lane);
+          O = mfma16x16x32(Ehi[ks], ph, O);
+          O = mfma16x16x32(Elo[ks], ph, O);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.Os[16 * mt + 4 * gq + r][vrow] = f2bf(p.scale * O[r]);
+        *(u32x2*)&sm.Os[16 * mt + n16][16 * wid + 4 * gq] =
+            u32x2{f2bf2(p.scale * O[0], p.scale * O[1]), f2bf2(p.scale * O[2], p.scale * O[3])};
       }
     }
 
@@ -610,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       if (pos % p.ckpt_every == 0 && pos > pre && pos <= pre + s.L) {
         const int j = pos / p.ckpt_every - pre / p.ckpt_every - 1;
         const int64_t row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + j, p.ckpt_idx64);
-        if (row >= 0) store_state(p.ckpt + row * p.ckpt_stride + head_off, accS);
+        if (row >= 0) store_state(p.ckpt + row * p.ckpt_stride + head_off, accS, gq);
       }
     }
     __syncthreads();  // every wave is done with this chunk's LDS operands
@@ -620,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     }
   }
   write_o(p, sm, s, nbase + kChunk * (nch - 1), tid);
-  if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS);
+  if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
 }
 
 // Longest-first order of the sequences (by chunk count; ties by index).
