@@ -29,7 +29,7 @@ constexpr int kFragElems = 64 * 8;  // one 16x16x32 MFMA operand fragment, bf16 
 // Per (chunk slot, v-head) record the intra-chunk kernel hands to the
 // recurrence: T = (I + A)^-1 as 8 hi + 8 lo bf16 operand fragments, and the
 // per-row scalars beta, G (log2 units), gamma = 2^G, exp(G_last - G).
-constexpr int kRecWords = 2 * 8 * kFragElems;  // bf16 elements (16 KiB)
+constexpr int kRecWords = 2 * 6 * kFragElems;  // bf16 elements (12 KiB): T's 6 nonzero fragments, hi and lo
 constexpr int kRecScal = 4 * kChunk;           // floats (1 KiB)
 
 struct PrefillParams {
@@ -44,6 +44,7 @@ struct PrefillParams {
   int32_t* order;  // [B] workspace: sequences longest first
   u16* ws_T;       // [chunk slots][H][kRecWords]
   float* ws_scal;  // [chunk slots][H][kRecScal]
+  u16* zero_row;   // 256 bytes (workspace), zeroed by the order kernel; read for padding rows
   int num_seqs;
   int H;
   int Hqk;

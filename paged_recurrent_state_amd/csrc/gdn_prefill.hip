@@ -43,6 +43,13 @@ constexpr int kKtWordsL = 8 * 2 * kFragElems;   // K^T fragments
 constexpr int kMatFrag = 8 * kFragElems;        // one 64x64 operand (8 fragments)
 constexpr int kAP = kChunk + 4;                 // fp32 row pitch of the 64x64 matrices
 
+// T is lower triangular: of its 8 operand fragments (row block mt, k-step
+// ks) the two with mt < 2, ks = 1 are zero.  The record keeps the other 6,
+// hi halves then lo halves.
+constexpr int kTFrags = 6;
+static_assert(kRecWords == 2 * kTFrags * kFragElems, "T record size");
+__device__ __forceinline__ int t_slot(int mt, int ks) { return mt < 2 ? mt : 2 * mt - 2 + ks; }
+
 // Fragment-ordered 64x128 tile: element (t, k) sits in fragment (t/16, k/32),
 // lane (t%16) + 16*gq, slot j, where k%32 = 16*(j/4) + 4*gq + j%4 (perm_row).
 // Offset (in bf16 elements) of the 4-run k..k+3 (k % 4 == 0) of row t.
@@ -76,6 +83,15 @@ __device__ __forceinline__ f32x4 mma3(const float (&a)[8], const float (&b)[8], 
 
 __device__ __forceinline__ bf16x8 lds_frag(const u16* base, int frag, int lane) {
   return *(const bf16x8*)(base + (frag * 64 + lane) * 8);
+}
+
+// Transposed 8-byte LDS read (16-bit elements): within each group of 16
+// lanes, lane 4a + e receives element e of the 4-element runs that lanes
+// a, 4 + a, 8 + a and 12 + a point at, in that order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // Lower-triangle block pair (i >= j) number blk (0..9) of the 4x4 block grid.
@@ -274,13 +290,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   }
   __syncthreads();
 
-  // T fragments (hi/lo) straight to the workspace
+  // T's 6 nonzero fragments (hi/lo) straight to the workspace
   u16* Tw = p.ws_T + ch * kRecWords;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int it = tid + kWyThreads * i;
     const int frag = it >> 6, ln = it & 63;
     const int mt = frag >> 1, ks = frag & 1;
+    if (mt < 2 && ks == 1) continue;  // all zero
     const int row = 16 * mt + (ln & 15), g4 = ln >> 4;
     float vals[8];
 #pragma unroll
@@ -291,33 +308,32 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     }
     bf16x8 hi, lo;
     split8(vals, hi, lo);
-    *(bf16x8*)(Tw + (frag * 64 + ln) * 8) = hi;
-    *(bf16x8*)(Tw + kMatFrag + (frag * 64 + ln) * 8) = lo;
+    const int slot = t_slot(mt, ks);
+    *(bf16x8*)(Tw + (slot * 64 + ln) * 8) = hi;
+    *(bf16x8*)(Tw + kTFrags * kFragElems + (slot * 64 + ln) * 8) = lo;
   }
 }
 
 // ============================================================== rec_kernel
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-
-// rec_kernel keeps its 64x128 tiles in plain fragment order: fragment
-// (t/16, k/32), lane (t%16) + 16*((k%32)/8), slot k%8 -- every 16-byte unit
-// is 8 consecutive k of one row, as it sits in memory.  The state's k index
-// is relabelled to match: accumulator block mb, lane group gq, row r holds
-// k = 32*(mb/2) + 8*gq + 4*(mb%2) + r, so blocks 2ks and 2ks+1 of a lane are
-// exactly the 8 consecutive k its B operand needs for k-step ks.
 constexpr int kOsPitch = kDim + 8;  // bf16 row pitch of the output tile
 
-struct RecSmem {
-  u16 Kf[kTileWords];     // K tile, plain fragment order
-  u16 Qf[kTileWords];     // Q tile
-  u16 Vf[kTileWords];     // V tile
-  u16 Ktf[kKtWordsL];     // K^T fragments: [k block][t-step][lane][8]
-  u16 Tf[2 * kMatFrag];   // T fragments, hi then lo (from wy_kernel)
-  u16 Pf[2 * kMatFrag];   // P fragments, hi then lo
-  u16 Os[kChunk][kOsPitch];  // output tile, written to memory after the chunk
-  float scal[4][kChunk];  // beta, G, gamma, exp(G_last - G)
-};
+// rec_kernel's 64x128 bf16 tiles are row-major in 16-byte units (8
+// consecutive k), unit k8 of row t at position t*16 + (k8 ^ (t % 8)): four
+// whole rows fill the 1 KiB that one global->LDS load writes (lane l to
+// position 64j + l), and the 8 lanes of an MFMA operand read (8 consecutive
+// t, one k8) meet 8 different bank quads.  The state's k index is
+// relabelled to match the operand layout: accumulator block mb, lane group
+// gq, row r holds k = 32*(mb/2) + 8*gq + 4*(mb%2) + r, so blocks 2ks and
+// 2ks+1 of a lane are exactly the 8 consecutive k its B operand needs for
+// k-step ks.
+__device__ __forceinline__ int tile_pos(int t, int k8) { return t * 16 + (k8 ^ (t & 7)); }
+
+// operand fragment f: lane (tt, gq) gets row 16*(f/4) + tt, k = 32*(f%4) + 8*gq ..
+__device__ __forceinline__ bf16x8 tile_frag(const u16* base, int f, int lane) {
+  return *(const bf16x8*)(base + tile_pos(16 * (f >> 2) + (lane & 15), 4 * (f & 3) + (lane >> 4)) * 8);
+}
 
 // k of accumulator row (block mb, lane group gq, r = 0)
 __device__ __forceinline__ int state_k(int mb, int gq) { return 32 * (mb >> 1) + 8 * gq + 4 * (mb & 1); }
@@ -328,62 +344,47 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&accS)[8], 
   for (int mb = 0; mb < 8; ++mb) *(f32x4*)(dst + state_k(mb, gq)) = accS[mb];
 }
 
-// Next chunk's inputs, held in registers while the current chunk computes.
-struct Prefetch {
-  u32x4 kq[4];  // two 16-byte units of the K tile, two of the Q tile
-  u32x4 v[2];   // two 16-byte units of the V tile
-  u32x4 tf[2];  // two 16-byte pieces of the T fragments
-  float sc;     // one scalar
+struct RecSmem {
+  u16 Kb[2][kTileWords];               // K tiles, double-buffered by chunk parity
+  u16 Qb[2][kTileWords];               // Q tiles
+  u16 Tf[2][2 * kTFrags * kFragElems]; // T fragments (wy_kernel's record), hi then lo
+  float scal[2][4][kChunk];            // beta, G, gamma, exp(G_last - G)
+  u16 Vb[kTileWords];                  // V tile (reloaded after the mid-chunk barrier)
+  u16 Ktf[kKtWordsL];                  // K^T fragments: [k block][t-step][lane][8]
+  u16 Pf[kMatFrag];                    // P fragments (bf16)
+  u16 Os[kChunk][kOsPitch];            // output tile, stored during the next chunk
 };
 
 struct Seq {
   int tok0, L, hq, h;
 };
 
-// Issue the loads of chunk slot c whose row 0 is new token n0.  Wave w, item
-// i fetches tile fragment 2w + i; its lane l takes row 16*(fragment/4) + l%16
-// and k-group 4*(fragment%4) + l/16 (16 rows x 64 contiguous bytes per
-// instruction).  Rows outside the sequence read token 0 of the sequence
-// (always in bounds); their values become zeros when stored to LDS, so
-// nothing here waits.
-__device__ __forceinline__ void load_chunk(Prefetch& pf, const PrefillParams& p, const Seq& s,
-                                           int64_t c, int n0, int tid) {
-  const int lane = tid & 63, wid = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int f = 2 * wid + i;
-    const int row = 16 * (f >> 2) + (lane & 15), seg = 4 * (f & 3) + (lane >> 4);
-    const int n = n0 + row;
-    const bool valid = (unsigned)n < (unsigned)s.L;
-    const int64_t tok = (int64_t)s.tok0 + (valid ? n : 0);
-    const int64_t off = (tok * p.Hqk + s.hq) * kDim + seg * 8;
-    pf.kq[i] = *(const u32x4*)(p.k + off);
-    pf.kq[2 + i] = *(const u32x4*)(p.q + off);
-    pf.v[i] = *(const u32x4*)(p.v + (tok * p.H + s.h) * kDim + seg * 8);
-  }
-  const int64_t ch = c * p.H + s.h;
-  const u16* Tw = p.ws_T + ch * kRecWords;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) pf.tf[i] = *(const u32x4*)(Tw + (tid + kThreads * i) * 8);
-  pf.sc = tid < kRecScal ? p.ws_scal[ch * kRecScal + tid] : 0.f;
+// One 16-byte global->LDS load a lane: lane l's bytes land at byte 16*l of
+// the instruction's 1 KiB destination block.
+__device__ __forceinline__ void lds_load16(u16* dst_block, const void* src) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst_block, 16, 0, 0);
 }
 
-__device__ __forceinline__ void store_chunk(const Prefetch& pf, RecSmem& sm, const Seq& s, int n0,
-                                            int tid) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  const int lane = tid & 63, wid = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int f = 2 * wid + i;
-    const int row = 16 * (f >> 2) + (lane & 15);
-    const bool valid = (unsigned)(n0 + row) < (unsigned)s.L;
-    const int at = (f * 64 + lane) * 8;  // consecutive lanes, consecutive 16 bytes
-    *(u32x4*)&sm.Kf[at] = valid ? pf.kq[i] : z;
-    *(u32x4*)&sm.Qf[at] = valid ? pf.kq[2 + i] : z;
-    *(u32x4*)&sm.Vf[at] = valid ? pf.v[i] : z;
-    *(u32x4*)&sm.Tf[(tid + kThreads * i) * 8] = pf.tf[i];
-  }
-  if (tid < kRecScal) (&sm.scal[0][0])[tid] = pf.sc;
+// Rows 4j..4j+3 of a token tile whose row 0 is new token n0 into block j of
+// `tile`.  Rows outside the sequence read 256 bytes of zeros (the padding
+// rows are exact identities of the recurrence).
+__device__ __forceinline__ void load_rows(u16* tile, const u16* src, int64_t stride, const u16* zero,
+                                          const Seq& s, int n0, int j, int lane) {
+  const int row = 4 * j + (lane >> 4);
+  const int n = n0 + row;
+  const int k8 = (lane & 15) ^ (row & 7);
+  const u16* rp = (unsigned)n < (unsigned)s.L ? src + ((int64_t)s.tok0 + n) * stride : zero;
+  lds_load16(tile + j * 512, rp + k8 * 8);
+}
+
+// T fragments and per-row scalars of chunk slot c (already in LDS order)
+__device__ __forceinline__ void load_rec(u16* Tdst, float* sdst, const PrefillParams& p, const Seq& s,
+                                         int64_t c, int wid, int lane) {
+  const int64_t ch = c * p.H + s.h;
+  const u16* Tw = p.ws_T + ch * kRecWords;
+  for (int j = wid; j < 2 * kTFrags; j += kWaves) lds_load16(Tdst + j * 512, Tw + j * 512 + lane * 8);
+  if (wid == kWaves - 1) lds_load16((u16*)sdst, p.ws_scal + ch * kRecScal + lane * 4);
 }
 
 // o rows of a finished chunk (row 0 = new token n0), 16-byte pieces.
@@ -399,6 +400,8 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
       *(u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + seg * 8) = w;
   }
 }
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -423,6 +426,20 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   const int wr = p.slots.write[b];
   const int vrow = 16 * wid + n16;
   const int64_t head_off = ((int64_t)s.h * kDim + vrow) * kDim;
+  const u16* ksrc = p.k + (int64_t)s.hq * kDim;
+  const u16* qsrc = p.q + (int64_t)s.hq * kDim;
+  const u16* vsrc = p.v + (int64_t)s.h * kDim;
+  const int64_t qk_stride = (int64_t)p.Hqk * kDim, v_stride = (int64_t)p.H * kDim;
+
+  const int nbase = (pre & ~(kChunk - 1)) - pre;  // new-token index of chunk 0's row 0
+  // chunk 0's inputs
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    load_rows(sm.Kb[0], ksrc, qk_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
+    load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
+    load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
+  }
+  load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, wid, lane);
 
   f32x4 accS[8];
   if (rd >= 0 && p.init) {
@@ -440,71 +457,36 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) vsel[j] = 8 * gq + j == 16 * (wid & 1) + n16 ? (__bf16)1.0f : (__bf16)0.0f;
 
-  const int nbase = (pre & ~(kChunk - 1)) - pre;  // new-token index of chunk 0's row 0
-  Prefetch pf;
-  load_chunk(pf, p, s, cs0, nbase, tid);
-  store_chunk(pf, sm, s, nbase, tid);
+  // P's blocks above the diagonal are zero for every chunk
+  for (int i = tid; i < kMatFrag / 4; i += kThreads) {  // 8-byte units: fragment, lane, half
+    const int f = i >> 7, ln = (i >> 1) & 63, half = i & 1;
+    const int bt = f >> 1, bs = 2 * (f & 1) + half;
+    if (bs > bt) *(u32x2*)&sm.Pf[(f * 64 + ln) * 8 + 4 * half] = u32x2{0u, 0u};
+  }
+  wait_loads();
   __syncthreads();
 
+  int64_t ckpt_row = -1;  // checkpoint of the previous chunk's end, stored one iteration late
   for (int ci = 0; ci < nch; ++ci) {
+    const int X = ci & 1;
     const int n0 = nbase + kChunk * ci;
-    if (ci + 1 < nch) load_chunk(pf, p, s, (int64_t)cs0 + ci + 1, n0 + kChunk, tid);
-    // o of the previous chunk leaves here, behind the prefetch loads, so the
-    // stores retire while this chunk computes (vector-memory counters retire
-    // in order; a store right before a wait would be waited for).
-    if (ci > 0) write_o(p, sm, s, n0 - kChunk, tid);
+    const bool more = ci + 1 < nch;
+    const u16* Kb = sm.Kb[X];
+    const u16* Qb = sm.Qb[X];
+    const u16* Tf = sm.Tf[X];
+    const float(*sc)[kChunk] = sm.scal[X];
 
-    // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
-    // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
-    // slots 4*(bs&1) + r of P fragment (bt, bs/2).  Written hi/lo; blocks
-    // above the diagonal are zero.  Wave w takes block pairs w and w + 8.
+    // The previous chunk's o and checkpoint leave while this chunk computes.
+    // The next chunk's loads go out in small groups spread over the
+    // iteration (K here, Q after Y, T after E, V after the mid-chunk
+    // barrier), so no wave sits long behind a full memory pipeline.
+    if (ci > 0) write_o(p, sm, s, n0 - kChunk, tid);
+    if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
+    if (more) {
 #pragma unroll
-    for (int pr = wid; pr < 16; pr += kWaves) {
-      const int bt = pr >> 2, bs = pr & 3;
-      uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
-      if (bs <= bt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = mfma16x16x32(lds_frag(sm.Kf, bs * 4 + ks, lane), lds_frag(sm.Qf, bt * 4 + ks, lane), acc);
-        const float Gt = sm.scal[1][16 * bt + n16];
-        const f32x4 Gs = *(const f32x4*)&sm.scal[1][16 * bs + 4 * gq];
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float val = exp2f(Gt - Gs[r]) * acc[r];
-          v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint32_t w = f2bf2(v[2 * i], v[2 * i + 1]);
-          hw[i] = w;
-          lw[i] = f2bf2(v[2 * i] - __uint_as_float(w << 16), v[2 * i + 1] - __uint_as_float(w & 0xffff0000u));
-        }
-      }
-      const int f = bt * 2 + (bs >> 1);
-      *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{hw[0], hw[1]};
-      *(u32x2*)&sm.Pf[kMatFrag + (f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{lw[0], lw[1]};
+      for (int i = 0; i < 2; ++i)
+        load_rows(sm.Kb[X ^ 1], ksrc, qk_stride, p.zero_row, s, n0 + kChunk, 2 * wid + i, lane);
     }
-    // K^T fragments: K[t][k] gathered from the K tile (rows k in the state's order)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int it = tid + kThreads * i;
-      const int frag = it >> 6, ln = it & 63;
-      const int mk = frag >> 1, ks = frag & 1;
-      const int kcol = state_k(mk, (ln & 15) >> 2) + (ln & 3), g4 = ln >> 4;
-      // offset of (row 0, kcol) in the plain fragment order
-      const int kin = ((kcol >> 5) * 64 + 16 * ((kcol & 31) >> 3)) * 8 + (kcol & 7);
-      u16 e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tt = perm_row(ks, g4, j);
-        e[j] = sm.Kf[kin + ((tt >> 4) * 4 * 64 + (tt & 15)) * 8];
-      }
-      *(u32x4*)&sm.Ktf[(frag * 64 + ln) * 8] =
-          u32x4{pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7])};
-    }
-    __syncthreads();
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
     bf16x8 Shi[4], Slo[4];
@@ -519,28 +501,32 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     // Y = K S^T, then R = beta (V - gamma Y); V's 16 columns enter through
     // the selection operand (exact: one product by 1 per element)
     f32x4 R[4];
-    {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 ak = lds_frag(sm.Kf, mt * 4 + ks, lane);
-          y = mfma16x16x32(ak, Shi[ks], y);
-          y = mfma16x16x32(ak, Slo[ks], y);
-        }
-        const f32x4 bt = *(const f32x4*)&sm.scal[0][16 * mt + 4 * gq];
-        const f32x4 gm = *(const f32x4*)&sm.scal[2][16 * mt + 4 * gq];
-        f32x4 c;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) c[r] = -gm[r] * y[r];
-        c = mfma16x16x32(lds_frag(sm.Vf, mt * 4 + (wid >> 1), lane), vsel, c);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) R[mt][r] = bt[r] * c[r];
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ak = tile_frag(Kb, mt * 4 + ks, lane);
+        y = mfma16x16x32(ak, Shi[ks], y);
+        y = mfma16x16x32(ak, Slo[ks], y);
       }
+      const f32x4 bt = *(const f32x4*)&sc[0][16 * mt + 4 * gq];
+      const f32x4 gm = *(const f32x4*)&sc[2][16 * mt + 4 * gq];
+      f32x4 c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[r] = -gm[r] * y[r];
+      c = mfma16x16x32(tile_frag(sm.Vb, mt * 4 + (wid >> 1), lane), vsel, c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[mt][r] = bt[r] * c[r];
     }
 
-    // E = T R
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        load_rows(sm.Qb[X ^ 1], qsrc, qk_stride, p.zero_row, s, n0 + kChunk, 2 * wid + i, lane);
+    }
+
+    // E = T R (T's row blocks 0 and 1 have no columns in k-step 1)
     f32x4 E[4];
     {
       bf16x8 Rhi[2], Rlo[2];
@@ -550,15 +536,67 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       for (int mt = 0; mt < 4; ++mt) {
         E[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int f = mt * 2 + ks;
-          const bf16x8 th = lds_frag(sm.Tf, f, lane);
-          const bf16x8 tl = lds_frag(sm.Tf + kMatFrag, f, lane);
+        for (int ks = 0; ks < (mt < 2 ? 1 : 2); ++ks) {
+          const int f = t_slot(mt, ks);
+          const bf16x8 th = lds_frag(Tf, f, lane);
+          const bf16x8 tl = lds_frag(Tf + kTFrags * kFragElems, f, lane);
           E[mt] = mfma16x16x32(th, Rhi[ks], E[mt]);
           E[mt] = mfma16x16x32(th, Rlo[ks], E[mt]);
           E[mt] = mfma16x16x32(tl, Rhi[ks], E[mt]);
         }
       }
+    }
+
+    if (more) load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid, lane);
+
+    // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
+    // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
+    // slots 4*(bs&1) + r of P fragment (bt, bs/2).  The ten blocks on and
+    // below the diagonal go to waves w and w + 8; the blocks above it stay
+    // at the zeros written before the first chunk.
+#pragma unroll
+    for (int blk = wid; blk < 10; blk += kWaves) {
+      const int bt = tri_i(blk), bs = tri_j(blk);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc);
+      const float Gt = sc[1][16 * bt + n16];
+      const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float val = exp2f(Gt - Gs[r]) * acc[r];
+        v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
+      }
+      const int f = bt * 2 + (bs >> 1);
+      *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
+    }
+    // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2) by
+    // transposed 8-byte LDS reads.  Within each 16-lane group g, source lane
+    // 4b + a points at K[t][state_k(mk, a) .. +3] with t = 32ks + 16hh + 4g + b,
+    // and the read returns to lane 4a + e the values K[t][state_k(mk, a) + e]
+    // for b = 0..3: A-operand slots 4hh + b of row state_k(mk, a) + e.
+    {
+      const int g = lane >> 4, b4 = (lane & 15) >> 2, a4 = lane & 3;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int f = wid + kWaves * i;
+        const int mk = f >> 1, ks = f & 1;
+        u32x2 half[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int t = 32 * ks + 16 * hh + 4 * g + b4;
+          half[hh] = lds_read_tr16(Kb + tile_pos(t, 4 * (mk >> 1) + a4) * 8 + 4 * (mk & 1));
+        }
+        *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] = u32x4{half[0].x, half[0].y, half[1].x, half[1].y};
+      }
+    }
+    __syncthreads();  // P and K^T complete; every wave is past its V reads
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, n0 + kChunk, 2 * wid + i, lane);
     }
 
     // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
@@ -571,17 +609,16 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         // output-only products: S Q^T with the state's hi part, E^T P^T
-        // without the E_lo P_lo-sized term (the bf16 output rounding
-        // dominates both)
+        // with P in bf16 (the bf16 output rounding dominates both)
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) z = mfma16x16x32(Shi[ks], lds_frag(sm.Qf, mt * 4 + ks, lane), z);
-        const float gm = sm.scal[2][16 * mt + n16];
+        for (int ks = 0; ks < 4; ++ks) z = mfma16x16x32(Shi[ks], tile_frag(Qb, mt * 4 + ks, lane), z);
+        const float gm = sc[2][16 * mt + n16];
         f32x4 O;
 #pragma unroll
         for (int r = 0; r < 4; ++r) O[r] = gm * z[r];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < (mt < 2 ? 1 : 2); ++ks) {
           const bf16x8 ph = lds_frag(sm.Pf, mt * 2 + ks, lane);
           O = mfma16x16x32(Ehi[ks], ph, O);
           O = mfma16x16x32(Elo[ks], ph, O);
@@ -593,11 +630,11 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
 
     // S <- gamma_last S + (dec E)^T K
     {
-      const float gC = sm.scal[2][kChunk - 1];
+      const float gC = sc[2][kChunk - 1];
       f32x4 Ed[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 dc = *(const f32x4*)&sm.scal[3][16 * mt + 4 * gq];
+        const f32x4 dc = *(const f32x4*)&sc[3][16 * mt + 4 * gq];
 #pragma unroll
         for (int r = 0; r < 4; ++r) Ed[mt][r] = dc[r] * E[mt][r];
       }
@@ -617,28 +654,29 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     }
 
     // checkpoint at this chunk's end?
+    ckpt_row = -1;
     if (p.ckpt_idx) {
       const int pos = (pre & ~(kChunk - 1)) + kChunk * (ci + 1);
       if (pos % p.ckpt_every == 0 && pos > pre && pos <= pre + s.L) {
         const int j = pos / p.ckpt_every - pre / p.ckpt_every - 1;
-        const int64_t row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + j, p.ckpt_idx64);
-        if (row >= 0) store_state(p.ckpt + row * p.ckpt_stride + head_off, accS, gq);
+        ckpt_row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + j, p.ckpt_idx64);
       }
     }
-    __syncthreads();  // every wave is done with this chunk's LDS operands
-    if (ci + 1 < nch) {
-      store_chunk(pf, sm, s, n0 + kChunk, tid);
-      __syncthreads();
-    }
+    wait_loads();     // the next chunk's tiles have landed (this wave's part)
+    __syncthreads();  // ... and every wave's; this chunk's LDS operands are free
   }
   write_o(p, sm, s, nbase + kChunk * (nch - 1), tid);
+  if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
   if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
 }
 
-// Longest-first order of the sequences (by chunk count; ties by index).
+// Longest-first order of the sequences (by chunk count; ties by index); also
+// clears the zero row that padding rows read.
 __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__ cu,
                                                      const int32_t* __restrict__ prefix, int B,
-                                                     int32_t* __restrict__ order) {
+                                                     int32_t* __restrict__ order,
+                                                     uint32_t* __restrict__ zero_row) {
+  if (threadIdx.x < 64) zero_row[threadIdx.x] = 0u;
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
     const int nb = chunks_of(prefix[b], cu[b + 1] - cu[b]);
     int rank = 0;
@@ -655,7 +693,8 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
-  order_kernel<<<1, 1024, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.num_seqs, p.order);
+  order_kernel<<<1, 1024, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.num_seqs, p.order,
+                                  (uint32_t*)p.zero_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   wy_kernel<<<dim3((unsigned)num_chunk_slots, (unsigned)p.H), kWyThreads, 0, s>>>(p);

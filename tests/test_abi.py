@@ -53,11 +53,11 @@ def test_workspace_size(lib):
     a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
     b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
     c = lib.gdn_prefill_workspace_size(64 * 100, 300, C.byref(d))
-    # rows + launch order per sequence, and one 17 KiB intra-chunk record per
+    # rows + launch order per sequence, and one 13 KiB intra-chunk record per
     # (chunk slot, v-head) with at most T/64 + 2B + 1 chunk slots
     assert 0 < a < b < c
     assert a % 256 == 0 and b % 256 == 0
-    assert b - a == 100 * 4 * (16384 + 1024)
+    assert b - a == 100 * 4 * (12288 + 1024)  # T record (6 fragments, hi and lo) + scalars
     bad = dims(K=64)
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
 
