@@ -39,13 +39,14 @@ int launched(hipError_t e, const char* what) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace: the per-sequence rows (5 x [B] int32), the launch order ([B]),
-// 256 bytes of zeros (read for padding rows) and, per (chunk slot, v-head),
-// the intra-chunk record (T fragments + scalars).
+// 256 bytes of zeros (read for padding rows), the chunk-slot table ([slots]
+// x 16 bytes) and, per (chunk slot, v-head), the intra-chunk record (T
+// fragments + scalars).
 // A sequence with L new tokens spans ceil(((prefix mod 64) + L) / 64) <=
 // (L + 126) / 64 chunks, so a batch never has more than T / 64 + 2 B of them.
 struct WsLayout {
   int64_t nc;
-  size_t slots, order, zero, T, scal, total;
+  size_t slots, order, zero, tab, T, scal, total;
 };
 
 WsLayout ws_layout(int64_t T, int B, int H) {
@@ -58,6 +59,8 @@ WsLayout ws_layout(int64_t T, int B, int H) {
   off += align256((size_t)B * sizeof(int32_t));
   w.zero = off;
   off += 256;
+  w.tab = off;
+  off += align256((size_t)w.nc * 4 * sizeof(int32_t));
   w.T = off;
   off += align256((size_t)w.nc * H * kRecWords * sizeof(u16));
   w.scal = off;
@@ -121,6 +124,8 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.cu_seqlens = cu;
   pp.slots = sd;
   pp.order = (int32_t*)((char*)ws + L.order);
+  pp.chunk_tab = (int4*)((char*)ws + L.tab);
+  pp.num_chunk_slots = (int)L.nc;
   pp.ws_T = (u16*)((char*)ws + L.T);
   pp.ws_scal = (float*)((char*)ws + L.scal);
   pp.zero_row = (u16*)((char*)ws + L.zero);

@@ -42,6 +42,8 @@ struct PrefillParams {
   const int32_t* cu_seqlens;
   SlotsDev slots;
   int32_t* order;  // [B] workspace: sequences longest first
+  int4* chunk_tab; // [chunk slots] workspace: {sequence (-1: unused), new-token index of row 0, L, first token}
+  int num_chunk_slots;
   u16* ws_T;       // [chunk slots][H][kRecWords]
   float* ws_scal;  // [chunk slots][H][kRecScal]
   u16* zero_row;   // 256 bytes (workspace), zeroed by the order kernel; read for padding rows

@@ -102,15 +102,59 @@ __device__ __forceinline__ int chunks_of(int prefix, int L) {
   return L > 0 ? ((prefix & (kChunk - 1)) + L + kChunk - 1) / kChunk : 0;
 }
 
+// The 64x128 bf16 token tiles are row-major in 16-byte units (8
+// consecutive k), unit k8 of row t at position t*16 + (k8 ^ (t % 8)): four
+// whole rows fill the 1 KiB that one global->LDS load writes (lane l to
+// position 64j + l), and the 8 lanes of an MFMA operand read (8 consecutive
+// t, one k8) meet 8 different bank quads.  The state's k index is
+// relabelled to match the operand layout: accumulator block mb, lane group
+// gq, row r holds k = 32*(mb/2) + 8*gq + 4*(mb%2) + r, so blocks 2ks and
+// 2ks+1 of a lane are exactly the 8 consecutive k its B operand needs for
+// k-step ks.
+__device__ __forceinline__ int tile_pos(int t, int k8) { return t * 16 + (k8 ^ (t & 7)); }
+
+// operand fragment f: lane (tt, gq) gets row 16*(f/4) + tt, k = 32*(f%4) + 8*gq ..
+__device__ __forceinline__ bf16x8 tile_frag(const u16* base, int f, int lane) {
+  return *(const bf16x8*)(base + tile_pos(16 * (f >> 2) + (lane & 15), 4 * (f & 3) + (lane >> 4)) * 8);
+}
+
+struct Seq {
+  int tok0, L, hq, h;
+};
+
+// One 16-byte global->LDS load a lane: lane l's bytes land at byte 16*l of
+// the instruction's 1 KiB destination block.
+__device__ __forceinline__ void lds_load16(u16* dst_block, const void* src) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst_block, 16, 0, 0);
+}
+
+// Rows 4j..4j+3 of a token tile whose row 0 is new token n0 into block j of
+// `tile`.  Rows outside the sequence read 256 bytes of zeros (the padding
+// rows are exact identities of the recurrence).
+__device__ __forceinline__ void load_rows(u16* tile, const u16* src, int64_t stride, const u16* zero,
+                                          const Seq& s, int n0, int j, int lane) {
+  const int row = 4 * j + (lane >> 4);
+  const int n = n0 + row;
+  const int k8 = (lane & 15) ^ (row & 7);
+  const u16* rp = (unsigned)n < (unsigned)s.L ? src + ((int64_t)s.tok0 + n) * stride : zero;
+  lds_load16(tile + j * 512, rp + k8 * 8);
+}
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ============================================================== wy_kernel
 constexpr int kWyThreads = 256;
 
 struct WySmem {
-  u16 Kf[kTileWords];
+  union {
+    u16 Kb[kTileWords];     // K tile (row-major, swizzled) ...
+    float T[kChunk][kAP];   // ... then T, once K K^T is done
+  } u;
   float A[kChunk][kAP];
-  float T[kChunk][kAP];
   float Xs[4][16][17];
-  int meta[4];
+  float G[kChunk];          // log2-scale running decay sum
+  float B[kChunk];          // beta (0 on padding rows)
 };
 
 __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
@@ -121,48 +165,24 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   const int lane = tid & 63, wid = tid >> 6;
   const int n16 = lane & 15, gq = lane >> 4;
 
-  // which sequence owns chunk slot c (one round of parallel loads per 256 sequences)
-  if (tid == 0) sm.meta[0] = -1;
-  __syncthreads();
-  for (int b = tid; b < p.num_seqs; b += kWyThreads) {
-    const int cs = p.slots.chunk_start[b];
-    if (cs <= c) {
-      const int t0 = p.cu_seqlens[b];
-      const int L = p.cu_seqlens[b + 1] - t0;
-      const int pre = p.slots.prefix[b];
-      if (c < cs + chunks_of(pre, L)) {
-        sm.meta[0] = b;
-        sm.meta[1] = (pre & ~(kChunk - 1)) + kChunk * (c - cs) - pre;  // row 0 -> new token idx
-        sm.meta[2] = L;
-        sm.meta[3] = t0;
-      }
-    }
-  }
-  __syncthreads();
-  if (sm.meta[0] < 0) return;  // slot beyond this batch's chunks (uniform exit)
-  const int n0 = sm.meta[1];
-  const int L = sm.meta[2];
-  const int tok0 = sm.meta[3];
-  const int hq = h / p.group;
+  const int4 e = p.chunk_tab[c];  // the same for every lane
+  if (e.x < 0) return;            // slot beyond this batch's chunks
+  Seq s;
+  s.L = e.z;
+  s.tok0 = e.w;
+  s.h = h;
+  s.hq = h / p.group;
+  const int n0 = e.y;
   const int64_t ch = (int64_t)c * p.H + h;
 
-  // K tile -> LDS in fragment order, rows outside the sequence zero
+  // K tile straight to LDS (padding rows read zeros), g and beta alongside
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int it = tid + kWyThreads * i;
-    const int row = it >> 4, k0 = (it & 15) * 8;
-    const int n = n0 + row;
-    const bool valid = (unsigned)n < (unsigned)L;
-    const u32x4 kv = *(const u32x4*)(p.k + (((int64_t)tok0 + (valid ? n : 0)) * p.Hqk + hq) * kDim + k0);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 w = valid ? kv : z;
-    *(u32x2*)&sm.Kf[tile_off(row, k0)] = u32x2{w.x, w.y};
-    *(u32x2*)&sm.Kf[tile_off(row, k0 + 4)] = u32x2{w.z, w.w};
-  }
-  // decay and beta, every wave (lane = row)
+  for (int i = 0; i < 4; ++i)
+    load_rows(sm.u.Kb, p.k + (int64_t)s.hq * kDim, (int64_t)p.Hqk * kDim, p.zero_row, s, n0,
+              4 * wid + i, lane);
   const int n = n0 + lane;
-  const bool valid = (unsigned)n < (unsigned)L;
-  const int64_t t = ((int64_t)tok0 + (valid ? n : 0)) * p.H + h;
+  const bool valid = (unsigned)n < (unsigned)s.L;
+  const int64_t t = ((int64_t)s.tok0 + (valid ? n : 0)) * p.H + h;
   const float gv = p.g ? p.g[t] : 0.f;
   const float bv = p.beta ? p.beta[t] : 1.f;
   float G = valid ? gv * kLog2e : 0.f;
@@ -172,14 +192,17 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     const float y = __shfl_up(G, off, 64);
     if (lane >= off) G += y;
   }
-  const float Glast = __shfl(G, 63, 64);
   if (wid == 0) {
+    const float Glast = __shfl(G, 63, 64);
     float* sc = p.ws_scal + ch * kRecScal;
     sc[lane] = bet;
     sc[kChunk + lane] = G;
     sc[2 * kChunk + lane] = exp2f(G);
     sc[3 * kChunk + lane] = exp2f(Glast - G);
+    sm.G[lane] = G;
+    sm.B[lane] = bet;
   }
+  wait_loads();
   __syncthreads();
 
   // K K^T lower blocks -> A = beta_row D k.k, strictly lower
@@ -188,17 +211,15 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      acc = mfma16x16x32(lds_frag(sm.Kf, bi * 4 + ks, lane), lds_frag(sm.Kf, bj * 4 + ks, lane), acc);
+      acc = mfma16x16x32(tile_frag(sm.u.Kb, bi * 4 + ks, lane), tile_frag(sm.u.Kb, bj * 4 + ks, lane), acc);
     const int col = 16 * bj + n16;
-    const float Gc = __shfl(G, col, 64);
-    // shuffles stay outside the masks: a lane-divergent bpermute reads 0 from
-    // inactive source lanes
+    const float Gc = sm.G[col];
+    const f32x4 Gr = *(const f32x4*)&sm.G[16 * bi + 4 * gq];
+    const f32x4 br = *(const f32x4*)&sm.B[16 * bi + 4 * gq];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * bi + 4 * gq + r;
-      const float Gr = __shfl(G, row, 64);
-      const float br = __shfl(bet, row, 64);
-      const float val = br * exp2f(Gr - Gc) * acc[r];
+      const float val = br[r] * exp2f(Gr[r] - Gc) * acc[r];
       sm.A[row][col] = row > col ? val : 0.f;
     }
   }
@@ -224,7 +245,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     }
     if (gq == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.T[16 * d + i][16 * d + col] = x[i];
+      for (int i = 0; i < 16; ++i) sm.u.T[16 * d + i][16 * d + col] = x[i];
     }
   }
   __syncthreads();
@@ -240,19 +261,19 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       a[j] = sm.A[16 * I + n16][16 * J + 4 * gq + j];
-      bb[j] = sm.T[16 * J + 4 * gq + j][16 * J + n16];
+      bb[j] = sm.u.T[16 * J + 4 * gq + j][16 * J + n16];
       a[j + 4] = 0.f;
       bb[j + 4] = 0.f;
     }
     const f32x4 X = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[j] = sm.T[16 * I + n16][16 * I + 4 * gq + j];
+      a[j] = sm.u.T[16 * I + n16][16 * I + 4 * gq + j];
       bb[j] = X[j];
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.T[16 * I + 4 * gq + r][16 * J + n16] = -Y[r];
+    for (int r = 0; r < 4; ++r) sm.u.T[16 * I + 4 * gq + r][16 * J + n16] = -Y[r];
   }
   __syncthreads();
   {
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
       const int kk = perm_row(0, gq, j);  // 0..31 over column blocks 0, 1
       const bool use = J == 0 || kk >= 16;  // T_01 = 0
       const float av = sm.A[16 * I + n16][kk];
-      const float tv = sm.T[kk][16 * J + n16];
+      const float tv = sm.u.T[kk][16 * J + n16];
       a[j] = use ? av : 0.f;
       bb[j] = use ? tv : 0.f;
     }
@@ -279,14 +300,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int j = 0; j < 8; ++j) {
       const int kk = perm_row(0, gq, j);  // 0..31 over rows/columns 32..63
       const bool use = I == 3 || kk < 16;  // T_23 = 0
-      const float tv = sm.T[16 * I + n16][32 + kk];
+      const float tv = sm.u.T[16 * I + n16][32 + kk];
       const float xv = sm.Xs[(kk >> 4) * 2 + J][kk & 15][n16];
       a[j] = use ? tv : 0.f;
       bb[j] = use ? xv : 0.f;
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.T[16 * I + 4 * gq + r][16 * J + n16] = -Y[r];
+    for (int r = 0; r < 4; ++r) sm.u.T[16 * I + 4 * gq + r][16 * J + n16] = -Y[r];
   }
   __syncthreads();
 
@@ -303,7 +324,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int cc = perm_row(ks, g4, j);
-      const float tv = sm.T[row][cc];
+      const float tv = sm.u.T[row][cc];
       vals[j] = cc <= row ? tv : 0.f;
     }
     bf16x8 hi, lo;
@@ -318,22 +339,6 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kOsPitch = kDim + 8;  // bf16 row pitch of the output tile
-
-// rec_kernel's 64x128 bf16 tiles are row-major in 16-byte units (8
-// consecutive k), unit k8 of row t at position t*16 + (k8 ^ (t % 8)): four
-// whole rows fill the 1 KiB that one global->LDS load writes (lane l to
-// position 64j + l), and the 8 lanes of an MFMA operand read (8 consecutive
-// t, one k8) meet 8 different bank quads.  The state's k index is
-// relabelled to match the operand layout: accumulator block mb, lane group
-// gq, row r holds k = 32*(mb/2) + 8*gq + 4*(mb%2) + r, so blocks 2ks and
-// 2ks+1 of a lane are exactly the 8 consecutive k its B operand needs for
-// k-step ks.
-__device__ __forceinline__ int tile_pos(int t, int k8) { return t * 16 + (k8 ^ (t & 7)); }
-
-// operand fragment f: lane (tt, gq) gets row 16*(f/4) + tt, k = 32*(f%4) + 8*gq ..
-__device__ __forceinline__ bf16x8 tile_frag(const u16* base, int f, int lane) {
-  return *(const bf16x8*)(base + tile_pos(16 * (f >> 2) + (lane & 15), 4 * (f & 3) + (lane >> 4)) * 8);
-}
 
 // k of accumulator row (block mb, lane group gq, r = 0)
 __device__ __forceinline__ int state_k(int mb, int gq) { return 32 * (mb >> 1) + 8 * gq + 4 * (mb & 1); }
@@ -354,29 +359,6 @@ struct RecSmem {
   u16 Pf[kMatFrag];                    // P fragments (bf16)
   u16 Os[kChunk][kOsPitch];            // output tile, stored during the next chunk
 };
-
-struct Seq {
-  int tok0, L, hq, h;
-};
-
-// One 16-byte global->LDS load a lane: lane l's bytes land at byte 16*l of
-// the instruction's 1 KiB destination block.
-__device__ __forceinline__ void lds_load16(u16* dst_block, const void* src) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst_block, 16, 0, 0);
-}
-
-// Rows 4j..4j+3 of a token tile whose row 0 is new token n0 into block j of
-// `tile`.  Rows outside the sequence read 256 bytes of zeros (the padding
-// rows are exact identities of the recurrence).
-__device__ __forceinline__ void load_rows(u16* tile, const u16* src, int64_t stride, const u16* zero,
-                                          const Seq& s, int n0, int j, int lane) {
-  const int row = 4 * j + (lane >> 4);
-  const int n = n0 + row;
-  const int k8 = (lane & 15) ^ (row & 7);
-  const u16* rp = (unsigned)n < (unsigned)s.L ? src + ((int64_t)s.tok0 + n) * stride : zero;
-  lds_load16(tile + j * 512, rp + k8 * 8);
-}
 
 // T fragments and per-row scalars of chunk slot c (already in LDS order)
 __device__ __forceinline__ void load_rec(u16* Tdst, float* sdst, const PrefillParams& p, const Seq& s,
@@ -401,7 +383,6 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
   }
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -670,21 +651,31 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
 }
 
-// Longest-first order of the sequences (by chunk count; ties by index); also
-// clears the zero row that padding rows read.
-__global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__ cu,
-                                                     const int32_t* __restrict__ prefix, int B,
-                                                     int32_t* __restrict__ order,
-                                                     uint32_t* __restrict__ zero_row) {
+// Launch plan, one workgroup: the longest-first order of the sequences (by
+// chunk count; ties by index), the chunk-slot table and the zero row that
+// padding rows read.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu,
+                                                    const int32_t* __restrict__ prefix,
+                                                    const int32_t* __restrict__ chunk_start, int B,
+                                                    int nslots, int32_t* __restrict__ order,
+                                                    int4* __restrict__ tab,
+                                                    uint32_t* __restrict__ zero_row) {
   if (threadIdx.x < 64) zero_row[threadIdx.x] = 0u;
+  for (int c = threadIdx.x; c < nslots; c += blockDim.x) tab[c] = int4{-1, 0, 0, 0};
+  __syncthreads();
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int nb = chunks_of(prefix[b], cu[b + 1] - cu[b]);
+    const int pre = prefix[b];
+    const int L = cu[b + 1] - cu[b];
+    const int nb = chunks_of(pre, L);
     int rank = 0;
     for (int o = 0; o < B; ++o) {
       const int no = chunks_of(prefix[o], cu[o + 1] - cu[o]);
       rank += (no > nb) || (no == nb && o < b);
     }
     order[rank] = b;
+    const int cs = chunk_start[b];
+    const int n0 = (pre & ~(kChunk - 1)) - pre;
+    for (int j = 0; j < nb && cs + j < nslots; ++j) tab[cs + j] = int4{b, n0 + kChunk * j, L, cu[b]};
   }
 }
 
@@ -693,8 +684,8 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
-  order_kernel<<<1, 1024, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.num_seqs, p.order,
-                                  (uint32_t*)p.zero_row);
+  plan_kernel<<<1, 1024, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs,
+                                 p.num_chunk_slots, p.order, p.chunk_tab, (uint32_t*)p.zero_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   wy_kernel<<<dim3((unsigned)num_chunk_slots, (unsigned)p.H), kWyThreads, 0, s>>>(p);

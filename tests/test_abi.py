@@ -57,7 +57,10 @@ def test_workspace_size(lib):
     # (chunk slot, v-head) with at most T/64 + 2B + 1 chunk slots
     assert 0 < a < b < c
     assert a % 256 == 0 and b % 256 == 0
-    assert b - a == 100 * 4 * (12288 + 1024)  # T record (6 fragments, hi and lo) + scalars
+    # T record (6 fragments, hi and lo) + scalars per (slot, head), and a
+    # 16-byte chunk-table entry per slot (regions rounded up to 256 bytes)
+    al = lambda x: (x + 255) // 256 * 256
+    assert b - a == 100 * 4 * (12288 + 1024) + al(103 * 16) - al(3 * 16)
     bad = dims(K=64)
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
 
