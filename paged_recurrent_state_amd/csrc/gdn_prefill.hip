@@ -85,33 +85,35 @@ __device__ __forceinline__ bf16x8 lds_frag(const u16* base, int frag, int lane) 
   return *(const bf16x8*)(base + (frag * 64 + lane) * 8);
 }
 
-// Transposed 8-byte LDS read (16-bit elements): within each group of 16
-// lanes, lane 4a + e receives element e of the 4-element runs that lanes
-// a, 4 + a, 8 + a and 12 + a point at, in that order.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  return __builtin_bit_cast(u32x2, r);
-}
-
 // Lower-triangle block pair (i >= j) number blk (0..9) of the 4x4 block grid.
 __device__ __forceinline__ int tri_i(int blk) { return blk >= 6 ? 3 : blk >= 3 ? 2 : blk >= 1 ? 1 : 0; }
 __device__ __forceinline__ int tri_j(int blk) { const int i = tri_i(blk); return blk - i * (i + 1) / 2; }
+
+// v-head of the j-th block of a sequence (or chunk).  Workgroups go to the
+// 8 XCDs round-robin by block index, so the g = H / Hqk v-heads that read the
+// same q/k head are placed 8 blocks apart: same XCD (and L2), dispatched
+// close together, so the second read of q and k hits in L2.  When H is not a
+// multiple of 8g the order is the identity.
+__device__ __forceinline__ int head_of(int j, int H, int g) {
+  if (g == 1 || H % (8 * g) != 0) return j;
+  const int qk = 8 * (j / (8 * g)) + (j & 7);
+  return qk * g + (j >> 3) % g;
+}
 
 __device__ __forceinline__ int chunks_of(int prefix, int L) {
   return L > 0 ? ((prefix & (kChunk - 1)) + L + kChunk - 1) / kChunk : 0;
 }
 
 // The 64x128 bf16 token tiles are row-major in 16-byte units (8
-// consecutive k), unit k8 of row t at position t*16 + (k8 ^ (t % 8)): four
+// consecutive k), unit k8 of row t at position t*16 + (k8 ^ (t % 16)): four
 // whole rows fill the 1 KiB that one global->LDS load writes (lane l to
-// position 64j + l), and the 8 lanes of an MFMA operand read (8 consecutive
-// t, one k8) meet 8 different bank quads.  The state's k index is
+// position 64j + l), and each 16-lane group of an MFMA operand read (16
+// consecutive t, one k8) covers all 16 four-bank groups of the 64 banks.  The state's k index is
 // relabelled to match the operand layout: accumulator block mb, lane group
 // gq, row r holds k = 32*(mb/2) + 8*gq + 4*(mb%2) + r, so blocks 2ks and
 // 2ks+1 of a lane are exactly the 8 consecutive k its B operand needs for
 // k-step ks.
-__device__ __forceinline__ int tile_pos(int t, int k8) { return t * 16 + (k8 ^ (t & 7)); }
+__device__ __forceinline__ int tile_pos(int t, int k8) { return t * 16 + (k8 ^ (t & 15)); }
 
 // operand fragment f: lane (tt, gq) gets row 16*(f/4) + tt, k = 32*(f%4) + 8*gq ..
 __device__ __forceinline__ bf16x8 tile_frag(const u16* base, int f, int lane) {
@@ -136,7 +138,7 @@ __device__ __forceinline__ void load_rows(u16* tile, const u16* src, int64_t str
                                           const Seq& s, int n0, int j, int lane) {
   const int row = 4 * j + (lane >> 4);
   const int n = n0 + row;
-  const int k8 = (lane & 15) ^ (row & 7);
+  const int k8 = (lane & 15) ^ (row & 15);
   const u16* rp = (unsigned)n < (unsigned)s.L ? src + ((int64_t)s.tok0 + n) * stride : zero;
   lds_load16(tile + j * 512, rp + k8 * 8);
 }
@@ -159,8 +161,8 @@ struct WySmem {
 
 __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   __shared__ __align__(16) WySmem sm;
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
+  const int c = blockIdx.x / p.H;
+  const int h = head_of(blockIdx.x - c * p.H, p.H, p.group);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int n16 = lane & 15, gq = lane >> 4;
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   const int item = blockIdx.x;
   const int b = p.order[item / p.H];
   Seq s;
-  s.h = item - (item / p.H) * p.H;
+  s.h = head_of(item - (item / p.H) * p.H, p.H, p.group);
   s.tok0 = p.cu_seqlens[b];
   s.L = p.cu_seqlens[b + 1] - s.tok0;
   if (s.L <= 0) return;  // a zero-length sequence writes nothing
@@ -437,6 +439,16 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   bf16x8 vsel;
 #pragma unroll
   for (int j = 0; j < 8; ++j) vsel[j] = 8 * gq + j == 16 * (wid & 1) + n16 ? (__bf16)1.0f : (__bf16)0.0f;
+
+  // 0/1 operands that pick, for lane column i, the k of accumulator row
+  // state_k(mk, i/4) + i%4 out of a 32-deep K fragment (mk%2 = h):
+  // B[8*gq + j][i] = 1 where gq == i/4 and j == 4h + i%4
+  bf16x8 ksel[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ksel[h][j] = gq == (n16 >> 2) && j == 4 * h + (n16 & 3) ? (__bf16)1.0f : (__bf16)0.0f;
 
   // P's blocks above the diagonal are zero for every chunk
   for (int i = tid; i < kMatFrag / 4; i += kThreads) {  // 8-byte units: fragment, lane, half
@@ -553,25 +565,19 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       const int f = bt * 2 + (bs >> 1);
       *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
     }
-    // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2) by
-    // transposed 8-byte LDS reads.  Within each 16-lane group g, source lane
-    // 4b + a points at K[t][state_k(mk, a) .. +3] with t = 32ks + 16hh + 4g + b,
-    // and the read returns to lane 4a + e the values K[t][state_k(mk, a) + e]
-    // for b = 0..3: A-operand slots 4hh + b of row state_k(mk, a) + e.
-    {
-      const int g = lane >> 4, b4 = (lane & 15) >> 2, a4 = lane & 3;
+    // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2): a K
+    // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
+    // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
+    // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int f = wid + kWaves * i;
-        const int mk = f >> 1, ks = f & 1;
-        u32x2 half[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int t = 32 * ks + 16 * hh + 4 * g + b4;
-          half[hh] = lds_read_tr16(Kb + tile_pos(t, 4 * (mk >> 1) + a4) * 8 + 4 * (mk & 1));
-        }
-        *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] = u32x4{half[0].x, half[0].y, half[1].x, half[1].y};
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int f = wid + kWaves * i;
+      const int mk = f >> 1, ks = f & 1;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
+      const f32x4 c2 = mfma16x16x32(tile_frag(Kb, (2 * ks + 1) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
+      *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] =
+          u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
     }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
     if (more) {
@@ -688,7 +694,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
                                  p.num_chunk_slots, p.order, p.chunk_tab, (uint32_t*)p.zero_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  wy_kernel<<<dim3((unsigned)num_chunk_slots, (unsigned)p.H), kWyThreads, 0, s>>>(p);
+  wy_kernel<<<(unsigned)(num_chunk_slots * p.H), kWyThreads, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   static bool attr_set = false;  // raised once per process; idempotent if raced
