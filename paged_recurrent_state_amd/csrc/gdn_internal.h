@@ -129,6 +129,8 @@ __device__ __forceinline__ uint32_t pack2(u16 lo, u16 hi) {
 }
 
 // Split 8 fp32 values into bf16 hi + lo parts (x ~= hi + lo to ~2^-17).
+// x = hi + lo with hi = bf16(x) (round to nearest) and lo = bf16(x - hi);
+// x - hi is exact in fp32.
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
   u32x4 h, l;
 #pragma unroll

@@ -125,11 +125,49 @@ struct Seq {
 };
 
 // One 16-byte global->LDS load a lane: lane l's bytes land at byte 16*l of
-// the instruction's 1 KiB destination block.
+// the instruction's 1 KiB destination block (M0 holds its LDS address).
+// Issued as inline assembly: these loads retire through the vector-memory
+// counter only, and hidden from the compiler they do not make it drain
+// every outstanding LDS read at each later wait.  Their completion is
+// awaited explicitly (wait_loads, then a barrier) before the data is read.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_load16(u16* dst_block, const void* src) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst_block, 16, 0, 0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst_block);
+  // (one wait state between the M0 write and the load that reads it)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+               : "memory", "m0");
 }
+// Same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void lds_load16_at(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a shared-memory pointer, as a wave-uniform value
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+// a pointer the whole wave agrees on, held in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Per-lane byte offset, from the first row of block j, of what lane l loads
+// in block j: row 4j + l/16, k-group (l%16) ^ (row%16).  Depends on j only
+// through j%4.
+__device__ __forceinline__ uint32_t tile_lane_off(int q, int lane, int64_t stride) {
+  const int r = lane >> 4;
+  const int k8 = (lane & 15) ^ ((4 * q + r) & 15);
+  return (uint32_t)(r * stride * 2 + k8 * 16);
+}
+
 
 // Rows 4j..4j+3 of a token tile whose row 0 is new token n0 into block j of
 // `tile`.  Rows outside the sequence read 256 bytes of zeros (the padding
@@ -143,7 +181,31 @@ __device__ __forceinline__ void load_rows(u16* tile, const u16* src, int64_t str
   lds_load16(tile + j * 512, rp + k8 * 8);
 }
 
+// Blocks j0 .. j0 + NB - 1 (j0 a multiple of 4) of a token tile whose row 0
+// is new token n0.  Chunks with every row inside the sequence take uniform
+// bases and the precomputed lane offsets; the first and last chunk of a
+// sequence check rows one by one.
+template <int NB>
+__device__ __forceinline__ void load_tile(u16* tile, const u16* src, int64_t stride,
+                                          const uint32_t (&voff)[4], const u16* zero, const Seq& s,
+                                          int n0, int j0, int lane) {
+  if (n0 >= 0 && n0 + kChunk <= s.L) {
+    const char* base = uniform_ptr(src + ((int64_t)s.tok0 + n0 + 4 * j0) * stride);
+    const uint32_t lds = lds_addr(tile + j0 * 512);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_load16_at(lds + i * 1024, base + (int64_t)i * 8 * stride, voff[i & 3]);
+  } else {
+#pragma unroll 1
+    for (int i = 0; i < NB; ++i) load_rows(tile, src, stride, zero, s, n0, j0 + i, lane);
+  }
+}
+
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Scheduling fence for hand-pipelined products: MFMAs and LDS accesses stay
+// on their side (so the next step's operand reads are in flight while this
+// step's MFMAs run); plain VALU and SALU work may move across.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0x6); }
 
 // ============================================================== wy_kernel
 constexpr int kWyThreads = 256;
@@ -221,7 +283,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * bi + 4 * gq + r;
-      const float val = br[r] * exp2f(Gr[r] - Gc) * acc[r];
+      const float val = br[r] * __builtin_amdgcn_exp2f(Gr[r] - Gc) * acc[r];
       sm.A[row][col] = row > col ? val : 0.f;
     }
   }
@@ -327,7 +389,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int j = 0; j < 8; ++j) {
       const int cc = perm_row(ks, g4, j);
       const float tv = sm.u.T[row][cc];
-      vals[j] = cc <= row ? tv : 0.f;
+      vals[j] = cc <= row ? tv * sm.B[cc] : 0.f;  // T diag(beta)
     }
     bf16x8 hi, lo;
     split8(vals, hi, lo);
@@ -362,22 +424,37 @@ struct RecSmem {
   u16 Os[kChunk][kOsPitch];            // output tile, stored during the next chunk
 };
 
-// T fragments and per-row scalars of chunk slot c (already in LDS order)
+// Half `part` (0 or 1) of the T fragments of chunk slot c (already in LDS
+// order), with the per-row scalars in half 0.
 __device__ __forceinline__ void load_rec(u16* Tdst, float* sdst, const PrefillParams& p, const Seq& s,
-                                         int64_t c, int wid, int lane) {
+                                         int64_t c, int part, int lane) {
   const int64_t ch = c * p.H + s.h;
-  const u16* Tw = p.ws_T + ch * kRecWords;
-  for (int j = wid; j < 2 * kTFrags; j += kWaves) lds_load16(Tdst + j * 512, Tw + j * 512 + lane * 8);
-  if (wid == kWaves - 1) lds_load16((u16*)sdst, p.ws_scal + ch * kRecScal + lane * 4);
+  const char* Tw = uniform_ptr(p.ws_T + ch * kRecWords + kTFrags * part * 512);
+  const uint32_t lds = lds_addr(Tdst + kTFrags * part * 512);
+#pragma unroll
+  for (int i = 0; i < kTFrags; ++i) lds_load16_at(lds + i * 1024, Tw + i * 1024, lane * 16);
+  if (part == 0) lds_load16_at(lds_addr(sdst), uniform_ptr(p.ws_scal + ch * kRecScal), lane * 16);
 }
 
-// o rows of a finished chunk (row 0 = new token n0), 16-byte pieces.
+// o rows 4j..4j+3 of a finished chunk (row 0 = new token n0), j = j0 ..
+// j0 + NJ - 1: 16 bytes a lane, 4 whole rows per store instruction.
+template <int NJ>
 __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& sm, const Seq& s,
-                                        int n0, int tid) {
+                                        int n0, int j0, int lane) {
+  if (n0 >= 0 && n0 + kChunk <= s.L) {  // every row inside the sequence
+    const int64_t rs = (int64_t)p.H * kDim * 2;  // o row stride, bytes
+    char* base = (char*)uniform_ptr(p.o + (((int64_t)s.tok0 + n0 + 4 * j0) * p.H + s.h) * kDim);
+    const uint32_t vo = (uint32_t)((lane >> 4) * rs + (lane & 15) * 16);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int it = tid + kThreads * i;
-    const int row = it >> 4, seg = it & 15;
+    for (int i = 0; i < NJ; ++i) {
+      const u32x4 w = *(const u32x4*)&sm.Os[4 * (j0 + i) + (lane >> 4)][(lane & 15) * 8];
+      *(u32x4*)(base + i * 4 * rs + vo) = w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int row = 4 * (j0 + i) + (lane >> 4), seg = lane & 15;
     const int nn = n0 + row;
     const u32x4 w = *(const u32x4*)&sm.Os[row][seg * 8];  // pitch keeps 16-byte alignment
     if ((unsigned)nn < (unsigned)s.L)
@@ -413,8 +490,15 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   const u16* qsrc = p.q + (int64_t)s.hq * kDim;
   const u16* vsrc = p.v + (int64_t)s.h * kDim;
   const int64_t qk_stride = (int64_t)p.Hqk * kDim, v_stride = (int64_t)p.H * kDim;
+  uint32_t off_qk[4], off_v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    off_qk[q] = tile_lane_off(q, lane, qk_stride);
+    off_v[q] = tile_lane_off(q, lane, v_stride);
+  }
 
   const int nbase = (pre & ~(kChunk - 1)) - pre;  // new-token index of chunk 0's row 0
+  const float log2_scale = __builtin_amdgcn_logf(p.scale);  // log2
   // chunk 0's inputs
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -422,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
     load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
   }
-  load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, wid, lane);
+  if (wid < 2) load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, wid, lane);
 
   f32x4 accS[8];
   if (rd >= 0 && p.init) {
@@ -469,17 +553,18 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     const u16* Tf = sm.Tf[X];
     const float(*sc)[kChunk] = sm.scal[X];
 
-    // The previous chunk's o and checkpoint leave while this chunk computes.
-    // The next chunk's loads go out in small groups spread over the
-    // iteration (K here, Q after Y, T after E, V after the mid-chunk
-    // barrier), so no wave sits long behind a full memory pipeline.
-    if (ci > 0) write_o(p, sm, s, n0 - kChunk, tid);
-    if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        load_rows(sm.Kb[X ^ 1], ksrc, qk_stride, p.zero_row, s, n0 + kChunk, 2 * wid + i, lane);
+    // Memory traffic of the iteration, by wave pairs at different points so
+    // that of the two waves sharing a SIMD (w and w + 4) one computes while
+    // the other waits to issue: at the top, waves 0-1 load the next K and
+    // waves 2-3 store the previous chunk's o; after Y, waves 4-5 load the
+    // next Q and waves 6-7 the next T; after the mid-chunk barrier, waves
+    // 4-7 load the next V.
+    if (wid < 2) {
+      if (more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
+    } else if (wid < 4) {
+      if (ci > 0) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
     }
+    if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
     bf16x8 Shi[4], Slo[4];
@@ -491,56 +576,76 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       split8(v, Shi[ks], Slo[ks]);
     }
 
-    // Y = K S^T, then R = beta (V - gamma Y); V's 16 columns enter through
-    // the selection operand (exact: one product by 1 per element)
+    // Y = K S^T, then R = V - gamma Y (beta is folded into the T record);
+    // V's 16 columns enter through the selection operand (exact: one product
+    // by 1 per element)
+    // (The products below keep 4 to 16 independent accumulators in flight:
+    // a chain of dependent MFMAs issues at about a third of the rate.)
     f32x4 R[4];
+    {
+    f32x4 y[4];
+    bf16x8 kf[2][4], vf[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      kf[0][mt] = tile_frag(Kb, mt * 4, lane);
+    }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ak = tile_frag(Kb, mt * 4 + ks, lane);
-        y = mfma16x16x32(ak, Shi[ks], y);
-        y = mfma16x16x32(ak, Slo[ks], y);
+    for (int ks = 0; ks < 4; ++ks) {
+      // operands of the next step (the V fragments after the last)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (ks < 3) kf[(ks + 1) & 1][mt] = tile_frag(Kb, mt * 4 + ks + 1, lane);
+        else vf[mt] = tile_frag(sm.Vb, mt * 4 + (wid >> 1), lane);
       }
-      const f32x4 bt = *(const f32x4*)&sc[0][16 * mt + 4 * gq];
+      sched_fence();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Shi[ks], y[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Slo[ks], y[mt]);
+      sched_fence();
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
       const f32x4 gm = *(const f32x4*)&sc[2][16 * mt + 4 * gq];
-      f32x4 c;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) c[r] = -gm[r] * y[r];
-      c = mfma16x16x32(tile_frag(sm.Vb, mt * 4 + (wid >> 1), lane), vsel, c);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) R[mt][r] = bt[r] * c[r];
+      for (int r = 0; r < 4; ++r) R[mt][r] = -gm[r] * y[mt][r];
+      R[mt] = mfma16x16x32(vf[mt], vsel, R[mt]);
+    }
     }
 
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        load_rows(sm.Qb[X ^ 1], qsrc, qk_stride, p.zero_row, s, n0 + kChunk, 2 * wid + i, lane);
+    if (more && wid >= 4) {
+      if (wid < 6) {
+        load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
+      } else {
+        load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid - 6, lane);
+      }
     }
 
-    // E = T R (T's row blocks 0 and 1 have no columns in k-step 1)
+    // E = (T diag(beta)) R (row blocks 0 and 1 have no columns in k-step 1)
     f32x4 E[4];
     {
       bf16x8 Rhi[2], Rlo[2];
       split_rows(R, 0, Rhi[0], Rlo[0]);
       split_rows(R, 1, Rhi[1], Rlo[1]);
+      bf16x8 th[kTFrags], tl[kTFrags];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        E[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < kTFrags; ++f) {
+        th[f] = lds_frag(Tf, f, lane);
+        tl[f] = lds_frag(Tf + kTFrags * kFragElems, f, lane);
+      }
 #pragma unroll
-        for (int ks = 0; ks < (mt < 2 ? 1 : 2); ++ks) {
-          const int f = t_slot(mt, ks);
-          const bf16x8 th = lds_frag(Tf, f, lane);
-          const bf16x8 tl = lds_frag(Tf + kTFrags * kFragElems, f, lane);
-          E[mt] = mfma16x16x32(th, Rhi[ks], E[mt]);
-          E[mt] = mfma16x16x32(th, Rlo[ks], E[mt]);
-          E[mt] = mfma16x16x32(tl, Rhi[ks], E[mt]);
-        }
+      for (int mt = 0; mt < 4; ++mt) E[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mt = ks ? 2 : 0; mt < 4; ++mt) E[mt] = mfma16x16x32(th[t_slot(mt, ks)], Rhi[ks], E[mt]);
+#pragma unroll
+        for (int mt = ks ? 2 : 0; mt < 4; ++mt) E[mt] = mfma16x16x32(th[t_slot(mt, ks)], Rlo[ks], E[mt]);
+#pragma unroll
+        for (int mt = ks ? 2 : 0; mt < 4; ++mt) E[mt] = mfma16x16x32(tl[t_slot(mt, ks)], Rhi[ks], E[mt]);
       }
     }
-
-    if (more) load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid, lane);
 
     // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
     // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
@@ -550,16 +655,19 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
 #pragma unroll
     for (int blk = wid; blk < 10; blk += kWaves) {
       const int bt = tri_i(blk), bs = tri_j(blk);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc);
-      const float Gt = sc[1][16 * bt + n16];
+      for (int ks = 0; ks < 4; ks += 2) {
+        acc0 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc0);
+        acc1 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks + 1, lane), tile_frag(Qb, bt * 4 + ks + 1, lane), acc1);
+      }
+      const f32x4 acc = acc0 + acc1;
+      const float Gt = sc[1][16 * bt + n16] + log2_scale;  // P carries the output scale
       const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float val = exp2f(Gt - Gs[r]) * acc[r];
+        const float val = __builtin_amdgcn_exp2f(Gt - Gs[r]) * acc[r];
         v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
       }
       const int f = bt * 2 + (bs >> 1);
@@ -580,38 +688,58 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
           u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
     }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, n0 + kChunk, 2 * wid + i, lane);
-    }
+    if (more && wid >= 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * (wid - 4), lane);
 
-    // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
-    // state fragments and E act as A operands, Q and P fragments as B, so a
-    // lane ends up with 4 adjacent v of one token (one 8-byte LDS store)
+    // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks (the
+    // scale rides on gamma here and on P's exponent): the state fragments
+    // and E act as A operands, Q and P fragments as B, so a lane ends up with
+    // 4 adjacent v of one token (one 8-byte LDS store)
     {
       bf16x8 Ehi[2], Elo[2];
       split_rows(E, 0, Ehi[0], Elo[0]);
       split_rows(E, 1, Ehi[1], Elo[1]);
+      // output-only products: S Q^T with the state's hi part, E^T P^T
+      // with P in bf16 (the bf16 output rounding dominates both)
+      f32x4 z[4];
+      bf16x8 qf[2][4], pfr[6];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        // output-only products: S Q^T with the state's hi part, E^T P^T
-        // with P in bf16 (the bf16 output rounding dominates both)
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qf[0][mt] = tile_frag(Qb, mt * 4, lane);
+      }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) z = mfma16x16x32(Shi[ks], tile_frag(Qb, mt * 4 + ks, lane), z);
-        const float gm = sc[2][16 * mt + n16];
-        f32x4 O;
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[r] = gm * z[r];
+          for (int mt = 0; mt < 4; ++mt) qf[(ks + 1) & 1][mt] = tile_frag(Qb, mt * 4 + ks + 1, lane);
+        } else {
+          // P fragments (mt, ks) with mt >= 2 or ks == 0: 0, 2, 4, 5, 6, 7
 #pragma unroll
-        for (int ks = 0; ks < (mt < 2 ? 1 : 2); ++ks) {
-          const bf16x8 ph = lds_frag(sm.Pf, mt * 2 + ks, lane);
-          O = mfma16x16x32(Ehi[ks], ph, O);
-          O = mfma16x16x32(Elo[ks], ph, O);
+          for (int i = 0; i < 6; ++i) pfr[i] = lds_frag(sm.Pf, i < 2 ? 2 * i : i + 2, lane);
         }
+        sched_fence();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Shi[ks], qf[ks & 1][mt], z[mt]);
+        sched_fence();
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float gm = p.scale * sc[2][16 * mt + n16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[mt][r] *= gm;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mt = ks ? 2 : 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Ehi[ks], pfr[t_slot(mt, ks)], z[mt]);
+#pragma unroll
+        for (int mt = ks ? 2 : 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Elo[ks], pfr[t_slot(mt, ks)], z[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 O = z[mt];
         *(u32x2*)&sm.Os[16 * mt + n16][16 * wid + 4 * gq] =
-            u32x2{f2bf2(p.scale * O[0], p.scale * O[1]), f2bf2(p.scale * O[2], p.scale * O[3])};
+            u32x2{f2bf2(O[0], O[1]), f2bf2(O[2], O[3])};
       }
     }
 
@@ -629,14 +757,26 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       split_rows(Ed, 0, Dhi[0], Dlo[0]);
       split_rows(Ed, 1, Dhi[1], Dlo[1]);
 #pragma unroll
-      for (int mk = 0; mk < 8; ++mk) {
-        accS[mk] = accS[mk] * gC;
+      for (int mk = 0; mk < 8; ++mk) accS[mk] = accS[mk] * gC;
+      // 4 groups (ks, mk/4) of 4 fragments, the next group read while this
+      // one multiplies (hi pass over the group's 4 blocks, then lo pass)
+      bf16x8 ktf[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 kt = lds_frag(sm.Ktf, mk * 2 + ks, lane);
-          accS[mk] = mfma16x16x32(kt, Dhi[ks], accS[mk]);
-          accS[mk] = mfma16x16x32(kt, Dlo[ks], accS[mk]);
+      for (int i = 0; i < 4; ++i) ktf[0][i] = lds_frag(sm.Ktf, i * 2, lane);
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int ks = gi >> 1, mk0 = 4 * (gi & 1);
+        if (gi < 3) {
+          const int nks = (gi + 1) >> 1, nmk0 = 4 * ((gi + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ktf[(gi + 1) & 1][i] = lds_frag(sm.Ktf, (nmk0 + i) * 2 + nks, lane);
         }
+        sched_fence();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accS[mk0 + i] = mfma16x16x32(ktf[gi & 1][i], Dhi[ks], accS[mk0 + i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accS[mk0 + i] = mfma16x16x32(ktf[gi & 1][i], Dlo[ks], accS[mk0 + i]);
+        sched_fence();
       }
     }
 
@@ -652,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     wait_loads();     // the next chunk's tiles have landed (this wave's part)
     __syncthreads();  // ... and every wave's; this chunk's LDS operands are free
   }
-  write_o(p, sm, s, nbase + kChunk * (nch - 1), tid);
+  write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
   if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
   if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
 }
