@@ -555,15 +555,11 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
 
     // Memory traffic of the iteration, by wave pairs at different points so
     // that of the two waves sharing a SIMD (w and w + 4) one computes while
-    // the other waits to issue: at the top, waves 0-1 load the next K and
-    // waves 2-3 store the previous chunk's o; after Y, waves 4-5 load the
-    // next Q and waves 6-7 the next T; after the mid-chunk barrier, waves
-    // 4-7 load the next V.
-    if (wid < 2) {
-      if (more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
-    } else if (wid < 4) {
-      if (ci > 0) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
-    }
+    // the other waits to issue: at the top, waves 0-1 load the next K; after
+    // Y, waves 2-3 store the previous chunk's o, waves 4-5 load the next Q
+    // and waves 6-7 the next T; after the mid-chunk barrier, waves 4-7 load
+    // the next V.
+    if (wid < 2 && more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
     if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
@@ -614,7 +610,9 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     }
     }
 
-    if (more && wid >= 4) {
+    if (wid == 2 || wid == 3) {
+      if (ci > 0) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
+    } else if (more && wid >= 4) {
       if (wid < 6) {
         load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
       } else {
