@@ -21,9 +21,12 @@ development; they print a line of the same form.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -47,11 +50,43 @@ def parse():
     ap.add_argument("--workload", default="hybrid", choices=["hybrid", "prefill", "decode", "long"])
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-sample-decode", type=int, default=128)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for "
                          "hardware byte counters); reported as copy_GBps")
     return ap.parse_args()
+
+
+# ----------------------------------------------------------------- measured traffic
+COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_counters__prefill_path_and_decode__hybrid_step.md")
+
+
+def kernel_sources_digest() -> str:
+    """sha256 (first 16 hex digits) of the HIP sources the counters were taken
+    on, with comments and whitespace removed (comment edits keep the digest)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "paged_recurrent_state_amd", "csrc", "*"))):
+        with open(f, encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        h.update(os.path.basename(f).encode() + b"\0" + code.encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    (copy-calibrated), or None when the kernel sources changed since."""
+    try:
+        text = open(COUNTERS_MD).read()
+    except OSError:
+        return None
+    m = re.search(r"bench-traffic: sources=([0-9a-f]+) prefill_path_bytes=(\d+) decode_bytes=(\d+)", text)
+    if not m or m.group(1) != kernel_sources_digest():
+        return None
+    return {"prefill": int(m.group(2)), "decode": int(m.group(3))}
 
 
 # ----------------------------------------------------------------- algorithmic work
@@ -73,8 +108,8 @@ def decode_bytes(B: int, H: int, Hqk: int) -> int:
 
 
 # ----------------------------------------------------------------- CPU baseline
-def cpu_baseline(pre_cpu, dec_cpu, pool_rows, sample_tokens, layers, step_prefill_tokens,
-                 step_decode_seqs):
+def cpu_baseline(pre_cpu, dec_cpu, pool_rows, sample_tokens, sample_decode, layers,
+                 step_prefill_tokens, step_decode_seqs):
     """Time the fp64 oracle on a bounded sample of layer 0 and scale to the step."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -96,8 +131,8 @@ def cpu_baseline(pre_cpu, dec_cpu, pool_rows, sample_tokens, layers, step_prefil
         ogdn.prefill(q, k, v, g, beta, [0, n], initial_state=Rows(),
                      state_indices=[rd], output_final_state=True, output_state_indices=[rd])
         t_pf = (time.perf_counter() - t0) / n
-        # decode sample: 32 sequences
-        m = 32
+        # decode sample: the first `sample_decode` sequences
+        m = sample_decode
         rows = dec_cpu["read_rows"][:m]
         t0 = time.perf_counter()
         ogdn.decode(dec_cpu["q"][:m], dec_cpu["k"][:m], dec_cpu["v"][:m], dec_cpu["g"][:m],
@@ -179,16 +214,21 @@ def hybrid(args, torch, gdn, workloads):
     dc_gbps = dc_bytes / (t_dc_ms / 1e3) / 1e9
     pf_tflops = prefill_flops(T, H) / (t_pf_ms / 1e3) / 1e12
 
+    # The dominant launch of the step: the prefill library call (three kernels
+    # on one stream: plan_kernel, wy_kernel, rec_kernel) or the decode call.
+    # achieved = algorithmic bytes per call / event-timed call duration.
+    traffic = measured_traffic() if L >= 2 else None
     if t_dc_ms >= t_pf_ms:
         roof = {"kernel": "decode_kernel", "bound": "hbm", "achieved": dc_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dc_gbps / HBM_PEAK_GBPS,
-                "traffic": None, "per_launch_bytes": dc_bytes, "avg_launch_ms": t_dc_ms}
+                "traffic": traffic and traffic["decode"], "per_launch_bytes": dc_bytes,
+                "avg_launch_ms": t_dc_ms}
     else:
         ach = pf_bytes / (t_pf_ms / 1e3) / 1e9
-        roof = {"kernel": "prefill_kernel", "bound": "hbm",
-                "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBPS, "traffic": None, "per_launch_bytes": pf_bytes,
-                "avg_launch_ms": t_pf_ms}
+        roof = {"kernel": "prefill path (plan_kernel + wy_kernel + rec_kernel, one call)",
+                "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBPS, "traffic": traffic and traffic["prefill"],
+                "per_launch_bytes": pf_bytes, "avg_launch_ms": t_pf_ms}
     real_prefill = int(c["num_prefill"])
     line = {
         "metric": METRIC,
@@ -218,7 +258,7 @@ def hybrid(args, torch, gdn, workloads):
         pcpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pre0.items()}
         pcpu["H"] = H
         dcpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dec0.items()}
-        rows = [pcpu["read_rows"][0]] + list(dcpu["read_rows"][:32])
+        rows = [pcpu["read_rows"][0]] + list(dcpu["read_rows"][:args.cpu_sample_decode])
         cpu_inputs = (pcpu, dcpu, rows, T, int(c["num_decode"]) + 16)
     return line, cpu_inputs, pool
 
@@ -353,7 +393,7 @@ def main():
         # timed steps rewrote them; the oracle's speed does not depend on their values.
         pool_rows = {int(r): pool[int(r)].cpu().numpy() for r in rows if int(r) >= 0}
         line["cpu_baseline"] = cpu_baseline(pcpu, dcpu, pool_rows, args.cpu_sample_tokens,
-                                            args.layers, T, ndec)
+                                            args.cpu_sample_decode, args.layers, T, ndec)
     if copy_gbps is not None:
         line["copy_GBps"] = copy_gbps
     print(json.dumps(line), flush=True)

@@ -16,21 +16,25 @@
 //   O = scale (diag(gamma) Q S0^T + P E),       P_ij = D_ij q_i.k_j (i >= j)
 //   S_end = gamma_last S0 + (diag(exp(G_last - G)) E)^T K
 //
+// plan_kernel: the longest-first sequence order, a table from chunk slot to
+//   (sequence, row-0 token) and a zeroed row that padding rows read.
 // wy_kernel (all chunks of the batch in parallel, one workgroup per chunk and
 //   v-head): K K^T on bf16 MFMA (exact products of bf16 inputs), the decay
 //   mask, and T by forward substitution in fp32 on the 16x16 diagonal blocks
 //   plus a two-level doubling on MFMA (hi/lo bf16 splits) for the
-//   off-diagonal blocks.  T leaves as ready-to-load MFMA fragments (hi and lo
-//   bf16 halves), with the per-row scalars beta, G, gamma and exp(G_last - G).
+//   off-diagonal blocks.  T diag(beta) leaves as ready-to-load MFMA fragments
+//   (hi and lo bf16 halves, the all-zero ones dropped), with the per-row
+//   scalars beta, G, gamma and exp(G_last - G).
 // rec_kernel (one workgroup per (sequence, v-head), longest sequences first):
 //   walks the chunks in order.  Per chunk, the P = D * (Q K^T) fragments come
 //   straight out of MFMA accumulators (computed as P^T blocks), K^T fragments
-//   are gathered from the K tile, and eight waves each advance 16 rows of the
-//   state, whose fp32 transpose lives in MFMA accumulators (the layout the
-//   next chunk's B operand needs).  fp32 operands are split into bf16 hi + lo
-//   (3 passes when both sides are fp32, 2 when one side is exact bf16), which
-//   keeps ~2^-17 relative accuracy.  The next chunk's inputs load into
-//   registers while the current one computes.
+//   come from K fragments times a 0/1 selection operand, and eight waves each
+//   advance 16 rows of the state, whose fp32 transpose lives in MFMA
+//   accumulators (the layout the next chunk's B operand needs).  fp32
+//   operands are split into bf16 hi + lo (3 passes when both sides are fp32,
+//   2 when one side is exact bf16), which keeps ~2^-17 relative accuracy.
+//   The next chunk's tiles load straight from global memory into
+//   double-buffered LDS while the current one computes.
 #include "gdn_internal.h"
 
 namespace gdn {
