@@ -45,7 +45,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileWords = 4 * 4 * kFragElems;  // 64 x 128 bf16, fragment order
 constexpr int kKtWordsL = 8 * 2 * kFragElems;   // K^T fragments
 constexpr int kMatFrag = 8 * kFragElems;        // one 64x64 operand (8 fragments)
-constexpr int kAP = kChunk + 4;                 // fp32 row pitch of the 64x64 matrices
 
 // T is lower triangular: of its 8 operand fragments (row block mt, k-step
 // ks) the two with mt < 2, ks = 1 are zero.  The record keeps the other 6,
@@ -214,15 +213,24 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // ============================================================== wy_kernel
 constexpr int kWyThreads = 256;
 
+// A and T are lower triangular: only their 10 blocks (bi >= bj) of 16x16
+// are kept, at a pitch of 20 floats (16-byte rows; the 4 row groups of an
+// MFMA result land in different banks).  tri_idx(bi, bj) of an upper block
+// still names one of the 10 (its contents are then masked off by the reader).
+constexpr int kBP = 20;
+__device__ __forceinline__ int tri_idx(int bi, int bj) { return bi * (bi + 1) / 2 + bj; }
+
 struct WySmem {
   union {
-    u16 Kb[kTileWords];     // K tile (row-major, swizzled) ...
-    float T[kChunk][kAP];   // ... then T, once K K^T is done
+    u16 Kb[kTileWords];        // K tile (row-major, swizzled) ...
+    struct {
+      float T[10][16][kBP];    // ... then T, once K K^T is done
+      float Xs[4][16][17];
+    } t;
   } u;
-  float A[kChunk][kAP];
-  float Xs[4][16][17];
-  float G[kChunk];          // log2-scale running decay sum
-  float B[kChunk];          // beta (0 on padding rows)
+  float A[10][16][kBP];
+  float G[kChunk];             // log2-scale running decay sum
+  float B[kChunk];             // beta (0 on padding rows)
 };
 
 __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * bi + 4 * gq + r;
       const float val = br[r] * __builtin_amdgcn_exp2f(Gr[r] - Gc) * acc[r];
-      sm.A[row][col] = row > col ? val : 0.f;
+      sm.A[blk][4 * gq + r][n16] = row > col ? val : 0.f;
     }
   }
   __syncthreads();
@@ -300,10 +308,11 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const f32x4 r0 = *(const f32x4*)&sm.A[16 * d + i][16 * d + 0];
-      const f32x4 r1 = *(const f32x4*)&sm.A[16 * d + i][16 * d + 4];
-      const f32x4 r2 = *(const f32x4*)&sm.A[16 * d + i][16 * d + 8];
-      const f32x4 r3 = *(const f32x4*)&sm.A[16 * d + i][16 * d + 12];
+      const float* Ar = sm.A[tri_idx(d, d)][i];
+      const f32x4 r0 = *(const f32x4*)(Ar + 0);
+      const f32x4 r1 = *(const f32x4*)(Ar + 4);
+      const f32x4 r2 = *(const f32x4*)(Ar + 8);
+      const f32x4 r3 = *(const f32x4*)(Ar + 12);
       const float a[16] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3],
                            r2[0], r2[1], r2[2], r2[3], r3[0], r3[1], r3[2], r3[3]};
       float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     }
     if (gq == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.T[16 * d + i][16 * d + col] = x[i];
+      for (int i = 0; i < 16; ++i) sm.u.t.T[tri_idx(d, d)][i][col] = x[i];
     }
   }
   __syncthreads();
@@ -328,20 +337,20 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     float a[8], bb[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[j] = sm.A[16 * I + n16][16 * J + 4 * gq + j];
-      bb[j] = sm.u.T[16 * J + 4 * gq + j][16 * J + n16];
+      a[j] = sm.A[tri_idx(I, J)][n16][4 * gq + j];
+      bb[j] = sm.u.t.T[tri_idx(J, J)][4 * gq + j][n16];
       a[j + 4] = 0.f;
       bb[j + 4] = 0.f;
     }
     const f32x4 X = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[j] = sm.u.T[16 * I + n16][16 * I + 4 * gq + j];
+      a[j] = sm.u.t.T[tri_idx(I, I)][n16][4 * gq + j];
       bb[j] = X[j];
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.u.T[16 * I + 4 * gq + r][16 * J + n16] = -Y[r];
+    for (int r = 0; r < 4; ++r) sm.u.t.T[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
   }
   __syncthreads();
   {
@@ -351,14 +360,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int j = 0; j < 8; ++j) {
       const int kk = perm_row(0, gq, j);  // 0..31 over column blocks 0, 1
       const bool use = J == 0 || kk >= 16;  // T_01 = 0
-      const float av = sm.A[16 * I + n16][kk];
-      const float tv = sm.u.T[kk][16 * J + n16];
+      const float av = sm.A[tri_idx(I, kk >> 4)][n16][kk & 15];
+      const float tv = sm.u.t.T[tri_idx(kk >> 4, J)][kk & 15][n16];
       a[j] = use ? av : 0.f;
       bb[j] = use ? tv : 0.f;
     }
     const f32x4 X = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Xs[wid][4 * gq + r][n16] = X[r];
+    for (int r = 0; r < 4; ++r) sm.u.t.Xs[wid][4 * gq + r][n16] = X[r];
   }
   __syncthreads();
   {
@@ -368,14 +377,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int j = 0; j < 8; ++j) {
       const int kk = perm_row(0, gq, j);  // 0..31 over rows/columns 32..63
       const bool use = I == 3 || kk < 16;  // T_23 = 0
-      const float tv = sm.u.T[16 * I + n16][32 + kk];
-      const float xv = sm.Xs[(kk >> 4) * 2 + J][kk & 15][n16];
+      const float tv = sm.u.t.T[tri_idx(I, 2 + (kk >> 4))][n16][kk & 15];
+      const float xv = sm.u.t.Xs[(kk >> 4) * 2 + J][kk & 15][n16];
       a[j] = use ? tv : 0.f;
       bb[j] = use ? xv : 0.f;
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.u.T[16 * I + 4 * gq + r][16 * J + n16] = -Y[r];
+    for (int r = 0; r < 4; ++r) sm.u.t.T[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
   }
   __syncthreads();
 
@@ -387,13 +396,17 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     const int frag = it >> 6, ln = it & 63;
     const int mt = frag >> 1, ks = frag & 1;
     if (mt < 2 && ks == 1) continue;  // all zero
-    const int row = 16 * mt + (ln & 15), g4 = ln >> 4;
+    const int rr = ln & 15, row = 16 * mt + rr, g4 = ln >> 4;
+    // slots 4h..4h+3: columns 32ks + 16h + 4g4 .. +3 of block (mt, 2ks + h)
     float vals[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int cc = perm_row(ks, g4, j);
-      const float tv = sm.u.T[row][cc];
-      vals[j] = cc <= row ? tv * sm.B[cc] : 0.f;  // T diag(beta)
+    for (int h = 0; h < 2; ++h) {
+      const int bj = 2 * ks + h, c0 = 16 * bj + 4 * g4;
+      const f32x4 tv = *(const f32x4*)&sm.u.t.T[tri_idx(mt, bj)][rr][4 * g4];
+      const f32x4 bv = *(const f32x4*)&sm.B[c0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vals[4 * h + e] = bj <= mt && c0 + e <= row ? tv[e] * bv[e] : 0.f;  // T diag(beta)
     }
     bf16x8 hi, lo;
     split8(vals, hi, lo);
@@ -567,6 +580,13 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
+    // Each MFMA run below has vector work beside it that does not depend on
+    // it, so the two can overlap: S's decay beside Y, R and its split beside
+    // Z = S Q^T, the z scaling beside E, E's splits beside the P and K^T
+    // products.  The products keep 4 to 16 independent accumulators in
+    // flight (a chain of dependent MFMAs issues at about a third of the
+    // rate), and each step's operand fragments are read while the previous
+    // step multiplies.
     bf16x8 Shi[4], Slo[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -576,42 +596,37 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       split8(v, Shi[ks], Slo[ks]);
     }
 
-    // Y = K S^T, then R = V - gamma Y (beta is folded into the T record);
-    // V's 16 columns enter through the selection operand (exact: one product
-    // by 1 per element)
-    // (The products below keep 4 to 16 independent accumulators in flight:
-    // a chain of dependent MFMAs issues at about a third of the rate.)
-    f32x4 R[4];
-    {
+    // Y = K S^T (hi and lo passes)
     f32x4 y[4];
-    bf16x8 kf[2][4], vf[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      kf[0][mt] = tile_frag(Kb, mt * 4, lane);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      // operands of the next step (the V fragments after the last)
+    bf16x8 vf[4];
+    {
+      bf16x8 kf[2][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        if (ks < 3) kf[(ks + 1) & 1][mt] = tile_frag(Kb, mt * 4 + ks + 1, lane);
-        else vf[mt] = tile_frag(sm.Vb, mt * 4 + (wid >> 1), lane);
+        y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        kf[0][mt] = tile_frag(Kb, mt * 4, lane);
       }
-      sched_fence();
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Shi[ks], y[mt]);
+      for (int ks = 0; ks < 4; ++ks) {
+        // operands of the next step (the V fragments after the last)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Slo[ks], y[mt]);
-      sched_fence();
+        for (int mt = 0; mt < 4; ++mt) {
+          if (ks < 3) kf[(ks + 1) & 1][mt] = tile_frag(Kb, mt * 4 + ks + 1, lane);
+          else vf[mt] = tile_frag(sm.Vb, mt * 4 + (wid >> 1), lane);
+        }
+        sched_fence();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Shi[ks], y[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Slo[ks], y[mt]);
+        sched_fence();
+      }
     }
+    // S's decay over the chunk (the update adds onto it at the end)
+    {
+      const float gC = sc[2][kChunk - 1];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const f32x4 gm = *(const f32x4*)&sc[2][16 * mt + 4 * gq];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) R[mt][r] = -gm[r] * y[mt][r];
-      R[mt] = mfma16x16x32(vf[mt], vsel, R[mt]);
-    }
+      for (int mk = 0; mk < 8; ++mk) accS[mk] = accS[mk] * gC;
     }
 
     if (wid == 2 || wid == 3) {
@@ -624,12 +639,47 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       }
     }
 
-    // E = (T diag(beta)) R (row blocks 0 and 1 have no columns in k-step 1)
-    f32x4 E[4];
+    // Z = S Q^T with the state's hi part (an output-only product: the bf16
+    // output rounding dominates its error); beside it R = V - gamma Y (beta
+    // is folded into the T record; V's 16 columns enter through the
+    // selection operand, exact) and R's hi/lo split
+    f32x4 z[4];
+    bf16x8 Rhi[2], Rlo[2];
     {
-      bf16x8 Rhi[2], Rlo[2];
+      bf16x8 qf[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        qf[0][mt] = tile_frag(Qb, mt * 4, lane);
+      }
+      f32x4 R[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 gm = *(const f32x4*)&sc[2][16 * mt + 4 * gq];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) R[mt][r] = -gm[r] * y[mt][r];
+        R[mt] = mfma16x16x32(vf[mt], vsel, R[mt]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) qf[(ks + 1) & 1][mt] = tile_frag(Qb, mt * 4 + ks + 1, lane);
+        }
+        sched_fence();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Shi[ks], qf[ks & 1][mt], z[mt]);
+        sched_fence();
+      }
       split_rows(R, 0, Rhi[0], Rlo[0]);
       split_rows(R, 1, Rhi[1], Rlo[1]);
+    }
+
+    // E = (T diag(beta)) R (row blocks 0 and 1 have no columns in k-step 1);
+    // beside it, z *= scale * gamma (the output scale rides on gamma here and
+    // on P's exponent)
+    f32x4 E[4];
+    {
       bf16x8 th[kTFrags], tl[kTFrags];
 #pragma unroll
       for (int f = 0; f < kTFrags; ++f) {
@@ -646,6 +696,12 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
         for (int mt = ks ? 2 : 0; mt < 4; ++mt) E[mt] = mfma16x16x32(th[t_slot(mt, ks)], Rlo[ks], E[mt]);
 #pragma unroll
         for (int mt = ks ? 2 : 0; mt < 4; ++mt) E[mt] = mfma16x16x32(tl[t_slot(mt, ks)], Rhi[ks], E[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float gm = p.scale * sc[2][16 * mt + n16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[mt][r] *= gm;
       }
     }
 
@@ -689,47 +745,33 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] =
           u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
     }
+    // E's splits (for P E and for the state update), beside the P and K^T
+    // products above
+    bf16x8 Ehi[2], Elo[2], Dhi[2], Dlo[2];
+    {
+      split_rows(E, 0, Ehi[0], Elo[0]);
+      split_rows(E, 1, Ehi[1], Elo[1]);
+      f32x4 Ed[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 dc = *(const f32x4*)&sc[3][16 * mt + 4 * gq];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ed[mt][r] = dc[r] * E[mt][r];
+      }
+      split_rows(Ed, 0, Dhi[0], Dlo[0]);
+      split_rows(Ed, 1, Dhi[1], Dlo[1]);
+    }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
     if (more && wid >= 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * (wid - 4), lane);
 
-    // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks (the
-    // scale rides on gamma here and on P's exponent): the state fragments
-    // and E act as A operands, Q and P fragments as B, so a lane ends up with
-    // 4 adjacent v of one token (one 8-byte LDS store)
+    // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
+    // state fragments and E act as A operands, Q and P fragments as B, so a
+    // lane ends up with 4 adjacent v of one token (one 8-byte LDS store)
     {
-      bf16x8 Ehi[2], Elo[2];
-      split_rows(E, 0, Ehi[0], Elo[0]);
-      split_rows(E, 1, Ehi[1], Elo[1]);
-      // output-only products: S Q^T with the state's hi part, E^T P^T
-      // with P in bf16 (the bf16 output rounding dominates both)
-      f32x4 z[4];
-      bf16x8 qf[2][4], pfr[6];
+      bf16x8 pfr[6];
+      // P fragments (mt, ks) with mt >= 2 or ks == 0: 0, 2, 4, 5, 6, 7
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        qf[0][mt] = tile_frag(Qb, mt * 4, lane);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < 3) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) qf[(ks + 1) & 1][mt] = tile_frag(Qb, mt * 4 + ks + 1, lane);
-        } else {
-          // P fragments (mt, ks) with mt >= 2 or ks == 0: 0, 2, 4, 5, 6, 7
-#pragma unroll
-          for (int i = 0; i < 6; ++i) pfr[i] = lds_frag(sm.Pf, i < 2 ? 2 * i : i + 2, lane);
-        }
-        sched_fence();
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Shi[ks], qf[ks & 1][mt], z[mt]);
-        sched_fence();
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const float gm = p.scale * sc[2][16 * mt + n16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[mt][r] *= gm;
-      }
+      for (int i = 0; i < 6; ++i) pfr[i] = lds_frag(sm.Pf, i < 2 ? 2 * i : i + 2, lane);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -738,30 +780,15 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
         for (int mt = ks ? 2 : 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Elo[ks], pfr[t_slot(mt, ks)], z[mt]);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 O = z[mt];
+      for (int mt = 0; mt < 4; ++mt)
         *(u32x2*)&sm.Os[16 * mt + n16][16 * wid + 4 * gq] =
-            u32x2{f2bf2(O[0], O[1]), f2bf2(O[2], O[3])};
-      }
+            u32x2{f2bf2(z[mt][0], z[mt][1]), f2bf2(z[mt][2], z[mt][3])};
     }
 
-    // S <- gamma_last S + (dec E)^T K
+    // S <- gamma_last S + (dec E)^T K (the decay was applied beside Y); 4
+    // groups (ks, mk/4) of 4 K^T fragments, the next group read while this
+    // one multiplies (hi pass over the group's 4 blocks, then lo pass)
     {
-      const float gC = sc[2][kChunk - 1];
-      f32x4 Ed[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 dc = *(const f32x4*)&sc[3][16 * mt + 4 * gq];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ed[mt][r] = dc[r] * E[mt][r];
-      }
-      bf16x8 Dhi[2], Dlo[2];
-      split_rows(Ed, 0, Dhi[0], Dlo[0]);
-      split_rows(Ed, 1, Dhi[1], Dlo[1]);
-#pragma unroll
-      for (int mk = 0; mk < 8; ++mk) accS[mk] = accS[mk] * gC;
-      // 4 groups (ks, mk/4) of 4 fragments, the next group read while this
-      // one multiplies (hi pass over the group's 4 blocks, then lo pass)
       bf16x8 ktf[2][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ktf[0][i] = lds_frag(sm.Ktf, i * 2, lane);
