@@ -12,9 +12,12 @@
 // last page in place); explicit mode takes index arrays.  A read row of -1
 // starts from literal zeros; a write row of -1 skips the store.
 //
-// Layout: one 256-thread workgroup per (sequence, head); each half-wave owns a
-// 512-byte state row at a time (32 lanes x 16 B, coalesced), 8 rows per
-// workgroup per step, all 16 steps' loads issued before any arithmetic.
+// Layout: one 256-thread workgroup per (sequence, head).  Each 16-lane group
+// owns one 512-byte state row at a time: lane c holds k = 4c..4c+3 and
+// 64+4c..64+4c+3, so one 16-byte load instruction covers 4 whole rows and
+// the row's dot products reduce inside the 16-lane group with 4 DPP steps
+// (no LDS traffic).  16 rows per workgroup per step, all 8 steps' loads
+// issued before any arithmetic.
 // Loads and stores bypass the caches' retention (non-temporal): every byte is
 // touched once.
 #include "gdn_internal.h"
@@ -24,15 +27,23 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerLane = kDim / 8;  // 16
+constexpr int kSteps = kDim / 16;  // 8: 16 rows per workgroup per step
 
 __device__ __forceinline__ int64_t ld_index(const void* p, int i, int idx64) {
   return idx64 ? ((const int64_t*)p)[i] : (int64_t)((const int32_t*)p)[i];
 }
 
-__device__ __forceinline__ float sum32(float x) {
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+// Sum over the 16 lanes of a DPP row, returned to all of them: swap
+// neighbours, swap pairs, mirror within 8, mirror within 16.
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<0xb1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4e>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
   return x;
 }
 
@@ -50,8 +61,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int half = lane >> 5;
-  const int kl = lane & 31;
+  const int g = lane >> 4;  // row within the wave's 4 rows of a step
+  const int c = lane & 15;  // k = 4c..4c+3 and 64+4c..64+4c+3
 
   int64_t rd, wr;
   if (p.mode == 1) {
@@ -66,47 +77,73 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   }
 
   const int hq = h / p.group;
-  float k4[4], q4[4];
-  unpack4(*(const u32x2*)(p.k + ((int64_t)b * p.Hqk + hq) * kDim + 4 * kl), k4);
-  unpack4(*(const u32x2*)(p.q + ((int64_t)b * p.Hqk + hq) * kDim + 4 * kl), q4);
+  float k8[8], q8[8];
+  {
+    const u16* kp = p.k + ((int64_t)b * p.Hqk + hq) * kDim + 4 * c;
+    const u16* qp = p.q + ((int64_t)b * p.Hqk + hq) * kDim + 4 * c;
+    float t[4];
+    unpack4(*(const u32x2*)kp, t);
+    for (int i = 0; i < 4; ++i) k8[i] = t[i];
+    unpack4(*(const u32x2*)(kp + 64), t);
+    for (int i = 0; i < 4; ++i) k8[4 + i] = t[i];
+    unpack4(*(const u32x2*)qp, t);
+    for (int i = 0; i < 4; ++i) q8[i] = t[i];
+    unpack4(*(const u32x2*)(qp + 64), t);
+    for (int i = 0; i < 4; ++i) q8[4 + i] = t[i];
+  }
   const int64_t bh = (int64_t)b * p.H + h;
   const float alpha = p.g ? expf(p.g[bh]) : 1.f;
   const float bt = p.beta ? p.beta[bh] : 1.f;
 
-  f32x4 s[kRowsPerLane];
+  // step it covers rows 16*it + 4*wid + g
+  f32x4 s[kSteps][2];
   if (rd >= 0) {
-    const float* src = p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * kl;
+    const float* src = p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * c;
 #pragma unroll
-    for (int it = 0; it < kRowsPerLane; ++it) {
-      const int row = it * 8 + wid * 2 + half;
-      s[it] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
+    for (int it = 0; it < kSteps; ++it) {
+      const int row = 16 * it + 4 * wid + g;
+      s[it][0] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
+      s[it][1] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim + 64));
     }
   } else {
 #pragma unroll
-    for (int it = 0; it < kRowsPerLane; ++it) s[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < kSteps; ++it) s[it][0] = s[it][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  float vv[kRowsPerLane];
+  float vv[kSteps];
 #pragma unroll
-  for (int it = 0; it < kRowsPerLane; ++it) vv[it] = bf2f(p.v[bh * kDim + it * 8 + wid * 2 + half]);
+  for (int it = 0; it < kSteps; ++it) vv[it] = bf2f(p.v[bh * kDim + 16 * it + 4 * wid + g]);
 
-  const float kq = sum32(k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3]);
-
-  float* dst = wr >= 0 ? p.out + wr * p.out_stride + (int64_t)h * kDim * kDim + 4 * kl : nullptr;
+  float kq = 0.f;
 #pragma unroll
-  for (int it = 0; it < kRowsPerLane; ++it) {
-    const int row = it * 8 + wid * 2 + half;
-    const f32x4 x = s[it];
-    float sk = x[0] * k4[0] + x[1] * k4[1] + x[2] * k4[2] + x[3] * k4[3];
-    float sq = x[0] * q4[0] + x[1] * q4[1] + x[2] * q4[2] + x[3] * q4[3];
-    sk = sum32(sk);
-    sq = sum32(sq);
+  for (int i = 0; i < 8; ++i) kq += k8[i] * q8[i];
+  kq = sum16(kq);
+
+  float* dst = wr >= 0 ? p.out + wr * p.out_stride + (int64_t)h * kDim * kDim + 4 * c : nullptr;
+  float o_mine = 0.f;  // o of row 16*c + 4*wid + g (lanes c < 8)
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int row = 16 * it + 4 * wid + g;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sk += s[it][hh][i] * k8[4 * hh + i];
+        sq += s[it][hh][i] * q8[4 * hh + i];
+      }
+    sk = sum16(sk);
+    sq = sum16(sq);
     const float delta = bt * (vv[it] - alpha * sk);
-    f32x4 y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = alpha * x[i] + delta * k4[i];
-    if (dst) __builtin_nontemporal_store(y, (f32x4*)(dst + row * kDim));
-    if (kl == 0) p.o[bh * kDim + row] = f2bf(p.scale * (alpha * sq + delta * kq));
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x4 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = alpha * s[it][hh][i] + delta * k8[4 * hh + i];
+      if (dst) __builtin_nontemporal_store(y, (f32x4*)(dst + row * kDim + 64 * hh));
+    }
+    if (c == it) o_mine = p.scale * (alpha * sq + delta * kq);
   }
+  if (c < kSteps) p.o[bh * kDim + 16 * c + 4 * wid + g] = f2bf(o_mine);
 }
 
 }  // namespace
