@@ -35,6 +35,8 @@
 //   2 when one side is exact bf16), which keeps ~2^-17 relative accuracy.
 //   The next chunk's tiles load straight from global memory into
 //   double-buffered LDS while the current one computes.
+#include <cstdlib>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -417,8 +419,9 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 }
 
 // ============================================================== rec_kernel
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+// A workgroup of NW waves advances NW x 16 state rows (a V-tile) of one
+// (sequence, v-head); with NW < 8 the 128 rows split over 8 / NW workgroups,
+// for batches too small to fill the chip with whole heads.
 constexpr int kOsPitch = kDim + 8;  // bf16 row pitch of the output tile
 
 // k of accumulator row (block mb, lane group gq, r = 0)
@@ -455,6 +458,23 @@ __device__ __forceinline__ void load_rec(u16* Tdst, float* sdst, const PrefillPa
 
 // o rows 4j..4j+3 of a finished chunk (row 0 = new token n0), j = j0 ..
 // j0 + NJ - 1: 16 bytes a lane, 4 whole rows per store instruction.
+// o rows of a finished chunk (row 0 = new token n0) for the workgroup's
+// columns v0 .. v0 + 16 NW - 1, all lanes of the workgroup: 16-byte units u =
+// tid + 64 NW i, row u / (2 NW), piece u % (2 NW).
+template <int NW>
+__device__ __forceinline__ void write_o_tile(const PrefillParams& p, const RecSmem& sm, const Seq& s,
+                                             int n0, int v0, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + 64 * NW * i;
+    const int row = u / (2 * NW), seg = u % (2 * NW);
+    const int nn = n0 + row;
+    const u32x4 w = *(const u32x4*)&sm.Os[row][seg * 8];
+    if ((unsigned)nn < (unsigned)s.L)
+      *(u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + v0 + seg * 8) = w;
+  }
+}
+
 template <int NJ>
 __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& sm, const Seq& s,
                                         int n0, int j0, int lane) {
@@ -480,18 +500,25 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
 }
 
 
-__global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kTiles = 8 / NW;  // V-tiles per head
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RecSmem& sm = *reinterpret_cast<RecSmem*>(smem_raw);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int n16 = lane & 15, gq = lane >> 4;
 
-  // Longest sequences first: blockIdx walks p.order (sorted by chunk count).
+  // Longest sequences first: blockIdx walks p.order (sorted by chunk count);
+  // the V-tiles of a head sit H blocks apart (same XCD when H % 8 == 0).
+  const int per_seq = p.H * kTiles;
   const int item = blockIdx.x;
-  const int b = p.order[item / p.H];
+  const int b = p.order[item / per_seq];
+  const int r_in = item - (item / per_seq) * per_seq;
+  const int vt = r_in / p.H;
   Seq s;
-  s.h = head_of(item - (item / p.H) * p.H, p.H, p.group);
+  s.h = head_of(r_in - vt * p.H, p.H, p.group);
   s.tok0 = p.cu_seqlens[b];
   s.L = p.cu_seqlens[b + 1] - s.tok0;
   if (s.L <= 0) return;  // a zero-length sequence writes nothing
@@ -501,7 +528,8 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   const int cs0 = p.slots.chunk_start[b];
   const int rd = p.slots.read[b];
   const int wr = p.slots.write[b];
-  const int vrow = 16 * wid + n16;
+  const int vb = vt * NW + wid;  // this wave's 16-row block of the state
+  const int vrow = 16 * vb + n16;
   const int64_t head_off = ((int64_t)s.h * kDim + vrow) * kDim;
   const u16* ksrc = p.k + (int64_t)s.hq * kDim;
   const u16* qsrc = p.q + (int64_t)s.hq * kDim;
@@ -517,13 +545,13 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   const int nbase = (pre & ~(kChunk - 1)) - pre;  // new-token index of chunk 0's row 0
   const float log2_scale = __builtin_amdgcn_logf(p.scale);  // log2
   // chunk 0's inputs
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    load_rows(sm.Kb[0], ksrc, qk_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
-    load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
-    load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, 2 * wid + i, lane);
+#pragma unroll 1
+  for (int j = wid; j < 16; j += NW) {
+    load_rows(sm.Kb[0], ksrc, qk_stride, p.zero_row, s, nbase, j, lane);
+    load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, j, lane);
+    load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, j, lane);
   }
-  if (wid < 2) load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, wid, lane);
+  for (int part = wid; part < 2; part += NW) load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, part, lane);
 
   f32x4 accS[8];
   if (rd >= 0 && p.init) {
@@ -536,10 +564,10 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
   }
 
   // 0/1 operand that picks this wave's 16 v columns out of a V fragment:
-  // B[8*gq + j][n] = 1 where 8*gq + j == 16*(wid%2) + n
+  // B[8*gq + j][n] = 1 where 8*gq + j == 16*(vb%2) + n
   bf16x8 vsel;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) vsel[j] = 8 * gq + j == 16 * (wid & 1) + n16 ? (__bf16)1.0f : (__bf16)0.0f;
+  for (int j = 0; j < 8; ++j) vsel[j] = 8 * gq + j == 16 * (vb & 1) + n16 ? (__bf16)1.0f : (__bf16)0.0f;
 
   // 0/1 operands that pick, for lane column i, the k of accumulator row
   // state_k(mk, i/4) + i%4 out of a 32-deep K fragment (mk%2 = h):
@@ -576,7 +604,13 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     // Y, waves 2-3 store the previous chunk's o, waves 4-5 load the next Q
     // and waves 6-7 the next T; after the mid-chunk barrier, waves 4-7 load
     // the next V.
-    if (wid < 2 && more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
+    if constexpr (NW == 8) {
+      if (wid < 2 && more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
+    } else if (more) {
+      // every wave loads 16 / NW consecutive blocks of the next K and Q
+      load_tile<16 / NW>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+      load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+    }
     if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
@@ -612,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           if (ks < 3) kf[(ks + 1) & 1][mt] = tile_frag(Kb, mt * 4 + ks + 1, lane);
-          else vf[mt] = tile_frag(sm.Vb, mt * 4 + (wid >> 1), lane);
+          else vf[mt] = tile_frag(sm.Vb, mt * 4 + (vb >> 1), lane);
         }
         sched_fence();
 #pragma unroll
@@ -629,13 +663,21 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       for (int mk = 0; mk < 8; ++mk) accS[mk] = accS[mk] * gC;
     }
 
-    if (wid == 2 || wid == 3) {
-      if (ci > 0) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
-    } else if (more && wid >= 4) {
-      if (wid < 6) {
-        load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
-      } else {
-        load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid - 6, lane);
+    if constexpr (NW == 8) {
+      if (wid == 2 || wid == 3) {
+        if (ci > 0) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
+      } else if (more && wid >= 4) {
+        if (wid < 6) {
+          load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
+        } else {
+          load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid - 6, lane);
+        }
+      }
+    } else {
+      if (ci > 0) write_o_tile<NW>(p, sm, s, n0 - kChunk, 16 * NW * vt, tid);
+      if (more) {
+        for (int part = wid; part < 2; part += NW)
+          load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, part, lane);
       }
     }
 
@@ -711,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     // below the diagonal go to waves w and w + 8; the blocks above it stay
     // at the zeros written before the first chunk.
 #pragma unroll
-    for (int blk = wid; blk < 10; blk += kWaves) {
+    for (int blk = wid; blk < 10; blk += NW) {
       const int bt = tri_i(blk), bs = tri_j(blk);
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
@@ -736,8 +778,8 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
     // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int f = wid + kWaves * i;
+    for (int i = 0; i < 16 / NW; ++i) {
+      const int f = wid + NW * i;
       const int mk = f >> 1, ks = f & 1;
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
@@ -762,7 +804,11 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
       split_rows(Ed, 1, Dhi[1], Dlo[1]);
     }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
-    if (more && wid >= 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * (wid - 4), lane);
+    if constexpr (NW == 8) {
+      if (more && wid >= 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * (wid - 4), lane);
+    } else if (more) {
+      load_tile<16 / NW>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+    }
 
     // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
     // state fragments and E act as A operands, Q and P fragments as B, so a
@@ -821,7 +867,8 @@ __global__ __launch_bounds__(kThreads) void rec_kernel(const PrefillParams p) {
     wait_loads();     // the next chunk's tiles have landed (this wave's part)
     __syncthreads();  // ... and every wave's; this chunk's LDS operands are free
   }
-  write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
+  if constexpr (NW == 8) write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
+  else write_o_tile<NW>(p, sm, s, nbase + kChunk * (nch - 1), 16 * NW * vt, tid);
   if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
   if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
 }
@@ -856,6 +903,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 
 }  // namespace
 
+template <int NW>
+hipError_t launch_rec(const PrefillParams& p, int64_t blocks, hipStream_t s) {
+  static bool attr_set = false;  // raised once per process and instance; idempotent if raced
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)rec_kernel<NW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RecSmem));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  rec_kernel<NW><<<(unsigned)blocks, NW * 64, sizeof(RecSmem), s>>>(p);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
@@ -866,14 +926,24 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   wy_kernel<<<(unsigned)(num_chunk_slots * p.H), kWyThreads, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static bool attr_set = false;  // raised once per process; idempotent if raced
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)rec_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sizeof(RecSmem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  // Whole heads per workgroup (8 waves).  Narrower V-tiles (4, 2 or 1
+  // waves) add workgroups but not speed: each still walks every chunk of its
+  // sequence, and the per-chunk time is set by the chunk's dependency chain,
+  // which fewer waves only lengthen (measured: a 32k-token single sequence,
+  // 32 heads, takes 2.28 / 2.32 / 2.68 / 3.69 ms with 8 / 4 / 2 / 1 waves).
+  // GDN_PREFILL_TILE_WAVES = 1, 2, 4 or 8 selects one (tests, tuning).
+  int nw = 8;
+  if (const char* f = getenv("GDN_PREFILL_TILE_WAVES")) {
+    const int v = atoi(f);
+    if (v == 1 || v == 2 || v == 4 || v == 8) nw = v;
   }
-  rec_kernel<<<(unsigned)blocks, kThreads, sizeof(RecSmem), s>>>(p);
+  switch (nw) {
+    case 8: e = launch_rec<8>(p, blocks, s); break;
+    case 4: e = launch_rec<4>(p, blocks * 2, s); break;
+    case 2: e = launch_rec<2>(p, blocks * 4, s); break;
+    default: e = launch_rec<1>(p, blocks * 8, s); break;
+  }
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

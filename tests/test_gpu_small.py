@@ -3,6 +3,7 @@ element, at sizes that span several chunks and ragged tails, plus the edge
 cases the pages define (empty, zero-length, -1 rows, page boundaries)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -316,3 +317,48 @@ def test_split_invariance_on_gpu():
     check_outputs(torch.cat(outs), o_ref[0])
     for r, s in o_ref[1].items():
         check_state(pool[r], s, f"page {r}")
+
+
+@pytest.mark.parametrize("waves", [8, 4, 2, 1])
+def test_prefill_every_tile_width(waves):
+    """The recurrence kernel in each of its V-tile widths (8, 4, 2 or 1 waves
+    per workgroup, forced): ragged sequences, GQA, slow decay, and a general
+    call with checkpoints."""
+    os.environ["GDN_PREFILL_TILE_WAVES"] = str(waves)
+    try:
+        pre, pool = make_case([0, 37, 128, 1], [130, 1, 64, 250], H=4, Hqk=2, seed=7, g_scale=0.3)
+        _, _, err = check_paged_prefill(pre, pool)
+        m = lib()
+        H = 2
+        N = 128
+        c = cuda(workloads.config3(heads=H, total=600, splits=(131, 400), every_n=N, num_rows=3))
+        ckpt = workloads.nan_pool(600 // N, H, 128, 128, device=DEV)
+        ref_slot = np.zeros((3, H, 128, 128))
+        ref_ck = {}
+        for call in c["calls"]:
+            o = m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
+                          call["cu_seqlens"], initial_state=c["pool"],
+                          state_indices=call["state_indices"], output_state=c["pool"],
+                          output_state_indices=call["output_state_indices"],
+                          output_final_state=True, state_checkpoints=ckpt,
+                          checkpoint_state_indices=c["checkpoint_state_indices"],
+                          checkpoint_cu_starts=call["checkpoint_cu_starts"],
+                          prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=N)
+            torch.cuda.synchronize()
+            res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(), call["g"].cpu(),
+                               call["beta"].cpu(), call["cu_seqlens"].cpu(), initial_state=ref_slot,
+                               state_indices=call["state_indices"].tolist(), output_final_state=True,
+                               output_state_indices=call["output_state_indices"].tolist(),
+                               checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
+                               checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
+                               prefix_lens=call["prefix_lens"].tolist(), checkpoint_every_n_tokens=N,
+                               shared_pool=False)
+            check_outputs(o, res.o)
+            ref_slot = ogdn.apply_writes(ref_slot, res.final)
+            ref_ck.update(res.checkpoints)
+            check_state(c["pool"][c["slot"]], ref_slot[c["slot"]], "slot")
+        for r, st in ref_ck.items():
+            check_state(ckpt[r], st, f"checkpoint {r}")
+        print(f"{waves} waves per workgroup: worst paged state rel {err:.2e}")
+    finally:
+        del os.environ["GDN_PREFILL_TILE_WAVES"]
