@@ -222,17 +222,18 @@ constexpr int kWyThreads = 256;
 constexpr int kBP = 20;
 __device__ __forceinline__ int tri_idx(int bi, int bj) { return bi * (bi + 1) / 2 + bj; }
 
+// The K tile's LDS is reused: once every wave holds its K K^T blocks in
+// registers, A is written over the tile, and each block of T is then formed
+// in place of the A block it replaces (every A block is read -- by the same
+// wave, or before a barrier -- before its T block is written).
 struct WySmem {
   union {
-    u16 Kb[kTileWords];        // K tile (row-major, swizzled) ...
-    struct {
-      float T[10][16][kBP];    // ... then T, once K K^T is done
-      float Xs[4][16][17];
-    } t;
+    u16 Kb[kTileWords];      // K tile (row-major, swizzled) ...
+    float AT[10][16][kBP];   // ... then A, turning into T block by block
   } u;
-  float A[10][16][kBP];
-  float G[kChunk];             // log2-scale running decay sum
-  float B[kChunk];             // beta (0 on padding rows)
+  float Xs[4][16][17];
+  float G[kChunk];           // log2-scale running decay sum
+  float B[kChunk];           // beta (0 on padding rows)
 };
 
 __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
@@ -283,22 +284,37 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   wait_loads();
   __syncthreads();
 
-  // K K^T lower blocks -> A = beta_row D k.k, strictly lower
-  for (int blk = wid; blk < 10; blk += 4) {
-    const int bi = tri_i(blk), bj = tri_j(blk);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // K K^T lower blocks -> A = beta_row D k.k, strictly lower: the blocks of
+  // wave w (w, w + 4, w + 8) stay in registers until every wave is done
+  // reading the K tile, then A goes over it.
+  f32x4 kk[3];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma16x16x32(tile_frag(sm.u.Kb, bi * 4 + ks, lane), tile_frag(sm.u.Kb, bj * 4 + ks, lane), acc);
-    const int col = 16 * bj + n16;
-    const float Gc = sm.G[col];
-    const f32x4 Gr = *(const f32x4*)&sm.G[16 * bi + 4 * gq];
-    const f32x4 br = *(const f32x4*)&sm.B[16 * bi + 4 * gq];
+  for (int i = 0; i < 3; ++i) {
+    const int blk = wid + 4 * i;
+    kk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (blk < 10) {
+      const int bi = tri_i(blk), bj = tri_j(blk);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * bi + 4 * gq + r;
-      const float val = br[r] * __builtin_amdgcn_exp2f(Gr[r] - Gc) * acc[r];
-      sm.A[blk][4 * gq + r][n16] = row > col ? val : 0.f;
+      for (int ks = 0; ks < 4; ++ks)
+        kk[i] = mfma16x16x32(tile_frag(sm.u.Kb, bi * 4 + ks, lane), tile_frag(sm.u.Kb, bj * 4 + ks, lane), kk[i]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int blk = wid + 4 * i;
+    if (blk < 10) {
+      const int bi = tri_i(blk), bj = tri_j(blk);
+      const int col = 16 * bj + n16;
+      const float Gc = sm.G[col];
+      const f32x4 Gr = *(const f32x4*)&sm.G[16 * bi + 4 * gq];
+      const f32x4 br = *(const f32x4*)&sm.B[16 * bi + 4 * gq];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * bi + 4 * gq + r;
+        const float val = br[r] * __builtin_amdgcn_exp2f(Gr[r] - Gc) * kk[i][r];
+        sm.u.AT[blk][4 * gq + r][n16] = row > col ? val : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -310,7 +326,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float* Ar = sm.A[tri_idx(d, d)][i];
+      const float* Ar = sm.u.AT[tri_idx(d, d)][i];
       const f32x4 r0 = *(const f32x4*)(Ar + 0);
       const f32x4 r1 = *(const f32x4*)(Ar + 4);
       const f32x4 r2 = *(const f32x4*)(Ar + 8);
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     }
     if (gq == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.t.T[tri_idx(d, d)][i][col] = x[i];
+      for (int i = 0; i < 16; ++i) sm.u.AT[tri_idx(d, d)][i][col] = x[i];
     }
   }
   __syncthreads();
@@ -339,20 +355,20 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     float a[8], bb[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[j] = sm.A[tri_idx(I, J)][n16][4 * gq + j];
-      bb[j] = sm.u.t.T[tri_idx(J, J)][4 * gq + j][n16];
+      a[j] = sm.u.AT[tri_idx(I, J)][n16][4 * gq + j];
+      bb[j] = sm.u.AT[tri_idx(J, J)][4 * gq + j][n16];
       a[j + 4] = 0.f;
       bb[j + 4] = 0.f;
     }
     const f32x4 X = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      a[j] = sm.u.t.T[tri_idx(I, I)][n16][4 * gq + j];
+      a[j] = sm.u.AT[tri_idx(I, I)][n16][4 * gq + j];
       bb[j] = X[j];
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.u.t.T[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
+    for (int r = 0; r < 4; ++r) sm.u.AT[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
   }
   __syncthreads();
   {
@@ -362,14 +378,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int j = 0; j < 8; ++j) {
       const int kk = perm_row(0, gq, j);  // 0..31 over column blocks 0, 1
       const bool use = J == 0 || kk >= 16;  // T_01 = 0
-      const float av = sm.A[tri_idx(I, kk >> 4)][n16][kk & 15];
-      const float tv = sm.u.t.T[tri_idx(kk >> 4, J)][kk & 15][n16];
+      const float av = sm.u.AT[tri_idx(I, kk >> 4)][n16][kk & 15];
+      const float tv = sm.u.AT[tri_idx(kk >> 4, J)][kk & 15][n16];
       a[j] = use ? av : 0.f;
       bb[j] = use ? tv : 0.f;
     }
     const f32x4 X = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.u.t.Xs[wid][4 * gq + r][n16] = X[r];
+    for (int r = 0; r < 4; ++r) sm.Xs[wid][4 * gq + r][n16] = X[r];
   }
   __syncthreads();
   {
@@ -379,14 +395,14 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     for (int j = 0; j < 8; ++j) {
       const int kk = perm_row(0, gq, j);  // 0..31 over rows/columns 32..63
       const bool use = I == 3 || kk < 16;  // T_23 = 0
-      const float tv = sm.u.t.T[tri_idx(I, 2 + (kk >> 4))][n16][kk & 15];
-      const float xv = sm.u.t.Xs[(kk >> 4) * 2 + J][kk & 15][n16];
+      const float tv = sm.u.AT[tri_idx(I, 2 + (kk >> 4))][n16][kk & 15];
+      const float xv = sm.Xs[(kk >> 4) * 2 + J][kk & 15][n16];
       a[j] = use ? tv : 0.f;
       bb[j] = use ? xv : 0.f;
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.u.t.T[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
+    for (int r = 0; r < 4; ++r) sm.u.AT[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
   }
   __syncthreads();
 
@@ -404,7 +420,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int bj = 2 * ks + h, c0 = 16 * bj + 4 * g4;
-      const f32x4 tv = *(const f32x4*)&sm.u.t.T[tri_idx(mt, bj)][rr][4 * g4];
+      const f32x4 tv = *(const f32x4*)&sm.u.AT[tri_idx(mt, bj)][rr][4 * g4];
       const f32x4 bv = *(const f32x4*)&sm.B[c0];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
