@@ -156,6 +156,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 
+// global-memory pointer (stores through it are global, not flat, stores)
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+
 // a pointer the whole wave agrees on, held in scalar registers
 __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
@@ -241,7 +245,8 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   const int c = blockIdx.x / p.H;
   const int h = head_of(blockIdx.x - c * p.H, p.H, p.group);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int n16 = lane & 15, gq = lane >> 4;
 
   const int4 e = p.chunk_tab[c];  // the same for every lane
@@ -496,13 +501,13 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
                                         int n0, int j0, int lane) {
   if (n0 >= 0 && n0 + kChunk <= s.L) {  // every row inside the sequence
     const int64_t rs = (int64_t)p.H * kDim * 2;  // o row stride, bytes
-    char* base = (char*)uniform_ptr(p.o + (((int64_t)s.tok0 + n0 + 4 * j0) * p.H + s.h) * kDim);
+    gptr<char> base = (gptr<char>)uniform_ptr(p.o + (((int64_t)s.tok0 + n0 + 4 * j0) * p.H + s.h) * kDim);
     const uint32_t vo = (uint32_t)((lane >> 4) * rs + (lane & 15) * 16);
+    u32x4 w[NJ];
 #pragma unroll
-    for (int i = 0; i < NJ; ++i) {
-      const u32x4 w = *(const u32x4*)&sm.Os[4 * (j0 + i) + (lane >> 4)][(lane & 15) * 8];
-      *(u32x4*)(base + i * 4 * rs + vo) = w;
-    }
+    for (int i = 0; i < NJ; ++i) w[i] = *(const u32x4*)&sm.Os[4 * (j0 + i) + (lane >> 4)][(lane & 15) * 8];
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) *(gptr<u32x4>)(base + i * 4 * rs + vo) = w[i];
     return;
   }
 #pragma unroll
@@ -523,7 +528,8 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RecSmem& sm = *reinterpret_cast<RecSmem*>(smem_raw);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
   const int n16 = lane & 15, gq = lane >> 4;
 
   // Longest sequences first: blockIdx walks p.order (sorted by chunk count);
@@ -605,6 +611,11 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   __syncthreads();
 
   int64_t ckpt_row = -1;  // checkpoint of the previous chunk's end, stored one iteration late
+  // the next checkpoint position (the first multiple of the interval past the
+  // prefix; chunk ends are multiples of 64, and so is the interval) and its
+  // index among the call's checkpoints of this sequence
+  int ck_next = p.ckpt_idx ? (pre / p.ckpt_every + 1) * p.ckpt_every : -1;
+  int ck_j = 0;
   for (int ci = 0; ci < nch; ++ci) {
     const int X = ci & 1;
     const int n0 = nbase + kChunk * ci;
@@ -628,6 +639,55 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
     if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
+
+    // P and K^T products (no dependence on the state): waves 4-7 run them at
+    // the top of the chunk, waves 0-3 after E, so that the two waves sharing
+    // a SIMD are at different points of the chain (one multiplying while the
+    // other does vector work).
+    auto pk_products = [&]() {
+      // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
+      // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
+      // slots 4*(bs&1) + r of P fragment (bt, bs/2).  The ten blocks on and
+      // below the diagonal go to waves w and w + 8; the blocks above it stay
+      // at the zeros written before the first chunk.
+#pragma unroll
+      for (int blk = wid; blk < 10; blk += NW) {
+        const int bt = tri_i(blk), bs = tri_j(blk);
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ks += 2) {
+          acc0 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc0);
+          acc1 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks + 1, lane), tile_frag(Qb, bt * 4 + ks + 1, lane), acc1);
+        }
+        const f32x4 acc = acc0 + acc1;
+        const float Gt = sc[1][16 * bt + n16] + log2_scale;  // P carries the output scale
+        const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float val = __builtin_amdgcn_exp2f(Gt - Gs[r]) * acc[r];
+          v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
+        }
+        const int f = bt * 2 + (bs >> 1);
+        *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
+      }
+      // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2): a K
+      // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
+      // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
+      // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
+#pragma unroll
+      for (int i = 0; i < 16 / NW; ++i) {
+        const int f = wid + NW * i;
+        const int mk = f >> 1, ks = f & 1;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
+        const f32x4 c2 = mfma16x16x32(tile_frag(Kb, (2 * ks + 1) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
+        *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] =
+            u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
+      }
+    };
+    constexpr bool kPkSplit = false;
+    if (kPkSplit && wid >= 4) pk_products();
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
     // Each MFMA run below has vector work beside it that does not depend on
@@ -763,46 +823,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       }
     }
 
-    // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
-    // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
-    // slots 4*(bs&1) + r of P fragment (bt, bs/2).  The ten blocks on and
-    // below the diagonal go to waves w and w + 8; the blocks above it stay
-    // at the zeros written before the first chunk.
-#pragma unroll
-    for (int blk = wid; blk < 10; blk += NW) {
-      const int bt = tri_i(blk), bs = tri_j(blk);
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-      for (int ks = 0; ks < 4; ks += 2) {
-        acc0 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc0);
-        acc1 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks + 1, lane), tile_frag(Qb, bt * 4 + ks + 1, lane), acc1);
-      }
-      const f32x4 acc = acc0 + acc1;
-      const float Gt = sc[1][16 * bt + n16] + log2_scale;  // P carries the output scale
-      const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float val = __builtin_amdgcn_exp2f(Gt - Gs[r]) * acc[r];
-        v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
-      }
-      const int f = bt * 2 + (bs >> 1);
-      *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
-    }
-    // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2): a K
-    // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
-    // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
-    // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
-#pragma unroll
-    for (int i = 0; i < 16 / NW; ++i) {
-      const int f = wid + NW * i;
-      const int mk = f >> 1, ks = f & 1;
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
-      const f32x4 c2 = mfma16x16x32(tile_frag(Kb, (2 * ks + 1) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
-      *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] =
-          u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
-    }
+    if (!(kPkSplit && wid >= 4)) pk_products();
     // E's splits (for P E and for the state update), beside the P and K^T
     // products above
     bf16x8 Ehi[2], Elo[2], Dhi[2], Dlo[2];
@@ -873,12 +894,10 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 
     // checkpoint at this chunk's end?
     ckpt_row = -1;
-    if (p.ckpt_idx) {
-      const int pos = (pre & ~(kChunk - 1)) + kChunk * (ci + 1);
-      if (pos % p.ckpt_every == 0 && pos > pre && pos <= pre + s.L) {
-        const int j = pos / p.ckpt_every - pre / p.ckpt_every - 1;
-        ckpt_row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + j, p.ckpt_idx64);
-      }
+    if ((pre & ~(kChunk - 1)) + kChunk * (ci + 1) == ck_next && ck_next <= pre + s.L) {
+      ckpt_row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + ck_j, p.ckpt_idx64);
+      ++ck_j;
+      ck_next += p.ckpt_every;
     }
     wait_loads();     // the next chunk's tiles have landed (this wave's part)
     __syncthreads();  // ... and every wave's; this chunk's LDS operands are free
