@@ -75,6 +75,14 @@ __device__ __forceinline__ void split_rows(const f32x4 (&x)[4], int ks, bf16x8& 
   split8(v, hi, lo);
 }
 
+// the same fragment rounded to bf16 (operand of an output-only product)
+__device__ __forceinline__ bf16x8 round_rows(const f32x4 (&x)[4], int ks) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = f2bf2(x[2 * ks + (i >> 1)][2 * (i & 1)], x[2 * ks + (i >> 1)][2 * (i & 1) + 1]);
+  return as_bf16x8(w);
+}
+
 // hi/lo 3-pass product of two fp32 operand fragments (~fp32 accuracy)
 __device__ __forceinline__ f32x4 mma3(const float (&a)[8], const float (&b)[8], f32x4 c) {
   bf16x8 ah, al, bh, bl;
@@ -824,12 +832,13 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     }
 
     if (!(kPkSplit && wid >= 4)) pk_products();
-    // E's splits (for P E and for the state update), beside the P and K^T
-    // products above
-    bf16x8 Ehi[2], Elo[2], Dhi[2], Dlo[2];
+    // E rounded to bf16 for P E (an output-only product, like Z: the bf16
+    // output rounding dominates its error) and (dec E) split hi/lo for the
+    // state update, beside the P and K^T products above
+    bf16x8 Ehi[2], Dhi[2], Dlo[2];
     {
-      split_rows(E, 0, Ehi[0], Elo[0]);
-      split_rows(E, 1, Ehi[1], Elo[1]);
+      Ehi[0] = round_rows(E, 0);
+      Ehi[1] = round_rows(E, 1);
       f32x4 Ed[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -859,8 +868,6 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int mt = ks ? 2 : 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Ehi[ks], pfr[t_slot(mt, ks)], z[mt]);
-#pragma unroll
-        for (int mt = ks ? 2 : 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Elo[ks], pfr[t_slot(mt, ks)], z[mt]);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
