@@ -637,7 +637,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     // that of the two waves sharing a SIMD (w and w + 4) one computes while
     // the other waits to issue: at the top, waves 0-1 load the next K; after
     // Y, waves 2-3 store the previous chunk's o, waves 4-5 load the next Q
-    // and waves 6-7 the next T; after the mid-chunk barrier, waves 4-7 load
+    // and waves 6-7 the next T; after the mid-chunk barrier, waves 0-3 load
     // the next V.
     if constexpr (NW == 8) {
       if (wid < 2 && more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
@@ -647,55 +647,6 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
     if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
-
-    // P and K^T products (no dependence on the state): waves 4-7 run them at
-    // the top of the chunk, waves 0-3 after E, so that the two waves sharing
-    // a SIMD are at different points of the chain (one multiplying while the
-    // other does vector work).
-    auto pk_products = [&]() {
-      // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
-      // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
-      // slots 4*(bs&1) + r of P fragment (bt, bs/2).  The ten blocks on and
-      // below the diagonal go to waves w and w + 8; the blocks above it stay
-      // at the zeros written before the first chunk.
-#pragma unroll
-      for (int blk = wid; blk < 10; blk += NW) {
-        const int bt = tri_i(blk), bs = tri_j(blk);
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-        for (int ks = 0; ks < 4; ks += 2) {
-          acc0 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc0);
-          acc1 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks + 1, lane), tile_frag(Qb, bt * 4 + ks + 1, lane), acc1);
-        }
-        const f32x4 acc = acc0 + acc1;
-        const float Gt = sc[1][16 * bt + n16] + log2_scale;  // P carries the output scale
-        const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float val = __builtin_amdgcn_exp2f(Gt - Gs[r]) * acc[r];
-          v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
-        }
-        const int f = bt * 2 + (bs >> 1);
-        *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
-      }
-      // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2): a K
-      // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
-      // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
-      // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
-#pragma unroll
-      for (int i = 0; i < 16 / NW; ++i) {
-        const int f = wid + NW * i;
-        const int mk = f >> 1, ks = f & 1;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
-        const f32x4 c2 = mfma16x16x32(tile_frag(Kb, (2 * ks + 1) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
-        *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] =
-            u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
-      }
-    };
-    constexpr bool kPkSplit = false;
-    if (kPkSplit && wid >= 4) pk_products();
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
     // Each MFMA run below has vector work beside it that does not depend on
@@ -831,7 +782,49 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       }
     }
 
-    if (!(kPkSplit && wid >= 4)) pk_products();
+    // P^T blocks (K rows x Q rows): the accumulator of block (t-block bt,
+    // s-block bs) holds, in lane (t, gq), P[16bt + t][16bs + 4gq + r] --
+    // slots 4*(bs&1) + r of P fragment (bt, bs/2).  The ten blocks on and
+    // below the diagonal: block w to wave w, and with 8 waves blocks 8 and 9
+    // to waves 2 and 3 (which have no loads of the next chunk to issue); the
+    // blocks above it stay at the zeros written before the first chunk.
+#pragma unroll
+    for (int bi = 0; bi < (NW == 8 ? 2 : (10 + NW - 1) / NW); ++bi) {
+      const int blk = NW == 8 ? (bi == 0 ? wid : (wid == 2 || wid == 3 ? wid + 6 : 10)) : wid + NW * bi;
+      if (blk >= 10) break;
+      const int bt = tri_i(blk), bs = tri_j(blk);
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+      for (int ks = 0; ks < 4; ks += 2) {
+        acc0 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc0);
+        acc1 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks + 1, lane), tile_frag(Qb, bt * 4 + ks + 1, lane), acc1);
+      }
+      const f32x4 acc = acc0 + acc1;
+      const float Gt = sc[1][16 * bt + n16] + log2_scale;  // P carries the output scale
+      const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float val = __builtin_amdgcn_exp2f(Gt - Gs[r]) * acc[r];
+        v[r] = 16 * bt + n16 >= 16 * bs + 4 * gq + r ? val : 0.f;
+      }
+      const int f = bt * 2 + (bs >> 1);
+      *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
+    }
+    // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2): a K
+    // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
+    // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
+    // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
+#pragma unroll
+    for (int i = 0; i < 16 / NW; ++i) {
+      const int f = wid + NW * i;
+      const int mk = f >> 1, ks = f & 1;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
+      const f32x4 c2 = mfma16x16x32(tile_frag(Kb, (2 * ks + 1) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
+      *(u32x4*)&sm.Ktf[(f * 64 + lane) * 8] =
+          u32x4{f2bf2(c1[0], c1[1]), f2bf2(c1[2], c1[3]), f2bf2(c2[0], c2[1]), f2bf2(c2[2], c2[3])};
+    }
     // E rounded to bf16 for P E (an output-only product, like Z: the bf16
     // output rounding dominates its error) and (dec E) split hi/lo for the
     // state update, beside the P and K^T products above
@@ -851,7 +844,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
     if constexpr (NW == 8) {
-      if (more && wid >= 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * (wid - 4), lane);
+      if (more && wid < 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * wid, lane);
     } else if (more) {
       load_tile<16 / NW>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
