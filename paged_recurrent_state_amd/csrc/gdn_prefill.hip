@@ -267,24 +267,28 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   const int n0 = e.y;
   const int64_t ch = (int64_t)c * p.H + h;
 
-  // K tile straight to LDS (padding rows read zeros), g and beta alongside
+  // K tile straight to LDS (padding rows read zeros); wave 0 loads g and
+  // beta alongside and scans the decay
+  {
+    const int64_t stride = (int64_t)p.Hqk * kDim;
+    uint32_t off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    load_rows(sm.u.Kb, p.k + (int64_t)s.hq * kDim, (int64_t)p.Hqk * kDim, p.zero_row, s, n0,
-              4 * wid + i, lane);
-  const int n = n0 + lane;
-  const bool valid = (unsigned)n < (unsigned)s.L;
-  const int64_t t = ((int64_t)s.tok0 + (valid ? n : 0)) * p.H + h;
-  const float gv = p.g ? p.g[t] : 0.f;
-  const float bv = p.beta ? p.beta[t] : 1.f;
-  float G = valid ? gv * kLog2e : 0.f;
-  const float bet = valid ? bv : 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(G, off, 64);
-    if (lane >= off) G += y;
+    for (int q = 0; q < 4; ++q) off[q] = tile_lane_off(q, lane, stride);
+    load_tile<4>(sm.u.Kb, p.k + (int64_t)s.hq * kDim, stride, off, p.zero_row, s, n0, 4 * wid, lane);
   }
   if (wid == 0) {
+    const int n = n0 + lane;
+    const bool valid = (unsigned)n < (unsigned)s.L;
+    const int64_t t = ((int64_t)s.tok0 + (valid ? n : 0)) * p.H + h;
+    const float gv = p.g ? p.g[t] : 0.f;
+    const float bv = p.beta ? p.beta[t] : 1.f;
+    float G = valid ? gv * kLog2e : 0.f;
+    const float bet = valid ? bv : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(G, off, 64);
+      if (lane >= off) G += y;
+    }
     const float Glast = __shfl(G, 63, 64);
     float* sc = p.ws_scal + ch * kRecScal;
     sc[lane] = bet;
@@ -332,10 +336,11 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   }
   __syncthreads();
 
-  // diagonal 16x16 blocks of (I + A)^-1 by forward substitution, wave d = block d
-  {
-    const int d = wid;
-    const int col = n16;  // lanes with gq > 0 compute duplicate columns
+  // diagonal 16x16 blocks of (I + A)^-1 by forward substitution, all four in
+  // wave 0: lane group d solves block d, one column a lane
+  if (wid == 0) {
+    const int d = gq;
+    const int col = n16;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -351,10 +356,8 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
       for (int j = 0; j < i; ++j) part[j & 3] += a[j] * x[j];
       x[i] = (i == col ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
     }
-    if (gq == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.AT[tri_idx(d, d)][i][col] = x[i];
-    }
+    for (int i = 0; i < 16; ++i) sm.u.AT[tri_idx(d, d)][i][col] = x[i];
   }
   __syncthreads();
 
