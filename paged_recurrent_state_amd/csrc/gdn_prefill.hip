@@ -426,27 +426,32 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   u16* Tw = p.ws_T + ch * kRecWords;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int it = tid + kWyThreads * i;
-    const int frag = it >> 6, ln = it & 63;
+    const int frag = wid + 4 * i;  // wave-uniform
     const int mt = frag >> 1, ks = frag & 1;
     if (mt < 2 && ks == 1) continue;  // all zero
-    const int rr = ln & 15, row = 16 * mt + rr, g4 = ln >> 4;
-    // slots 4h..4h+3: columns 32ks + 16h + 4g4 .. +3 of block (mt, 2ks + h)
+    const int rr = lane & 15, g4 = lane >> 4;
+    // slots 4h..4h+3: columns 32ks + 16h + 4g4 .. +3 of block (mt, 2ks + h);
+    // blocks above the diagonal are zero, and so is the upper triangle of
+    // the diagonal blocks (exactly, from the substitution)
     float vals[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int bj = 2 * ks + h, c0 = 16 * bj + 4 * g4;
-      const f32x4 tv = *(const f32x4*)&sm.u.AT[tri_idx(mt, bj)][rr][4 * g4];
-      const f32x4 bv = *(const f32x4*)&sm.B[c0];
+      if (bj <= mt) {
+        const f32x4 tv = *(const f32x4*)&sm.u.AT[tri_idx(mt, bj)][rr][4 * g4];
+        const f32x4 bv = *(const f32x4*)&sm.B[c0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vals[4 * h + e] = bj <= mt && c0 + e <= row ? tv[e] * bv[e] : 0.f;  // T diag(beta)
+        for (int e = 0; e < 4; ++e) vals[4 * h + e] = tv[e] * bv[e];  // T diag(beta)
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[4 * h + e] = 0.f;
+      }
     }
     bf16x8 hi, lo;
     split8(vals, hi, lo);
     const int slot = t_slot(mt, ks);
-    *(bf16x8*)(Tw + (slot * 64 + ln) * 8) = hi;
-    *(bf16x8*)(Tw + kTFrags * kFragElems + (slot * 64 + ln) * 8) = lo;
+    *(bf16x8*)(Tw + (slot * 64 + lane) * 8) = hi;
+    *(bf16x8*)(Tw + kTFrags * kFragElems + (slot * 64 + lane) * 8) = lo;
   }
 }
 
