@@ -228,6 +228,59 @@ int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void*
                int64_t output_row_stride, const void* output_state_indices,
                int32_t index_dtype, void* o, hipStream_t stream);
 
+/*
+ * gdn_block_table_to_csr -- padded block table -> the CSR page table the
+ * paged calls take, on the device, in two launches and without a host
+ * synchronization (FlashInfer CSR paging drill, section 2: a sequence of ctx
+ * tokens owns ceil(ctx / page_size) pages; indptr is the running sum of those
+ * counts with indptr[0] = 0; the indices are the first that many entries of
+ * every row, rows in order; the last page holds ctx - (pages - 1) * page_size
+ * tokens, 1 .. page_size).
+ *   block_tables  [num_seqs, row_stride] int32 device array; only the first
+ *                 ceil(ctx_lens[b] / page_size) entries of row b are read.
+ *   ctx_lens      [num_seqs] int32 device array, tokens per sequence.
+ *   max_blocks    columns a row may use (<= row_stride).
+ *   page_indptr   [num_seqs + 1] int32 device array, written.
+ *   page_indices  int32 device array with room for num_seqs * max_blocks
+ *                 entries; the first page_indptr[num_seqs] are written.
+ *   last_page_len [num_seqs] int32 device array, written.
+ *   bad_rows      optional [1] int32 device array, written: the number of
+ *                 rows the CSR form cannot hold (ctx_lens < 1, or more than
+ *                 max_blocks pages).  Such rows get no pages and
+ *                 last_page_len 0; a table with bad rows must not be passed to
+ *                 the paged calls.
+ * Errors: GDN_EINVAL for null pointers, num_seqs < 0, page_size <= 0,
+ * max_blocks < 0 or row_stride < max_blocks.
+ */
+int gdn_block_table_to_csr(const int32_t* block_tables, int64_t row_stride,
+                           const int32_t* ctx_lens, int32_t num_seqs, int32_t max_blocks,
+                           int32_t page_size, int32_t* page_indptr, int32_t* page_indices,
+                           int32_t* last_page_len, int32_t* bad_rows, hipStream_t stream);
+
+/*
+ * gdn_csr_to_block_table -- CSR page table -> padded block table and context
+ * lengths, on the device, without a host synchronization (FlashInfer CSR
+ * paging drill, section 3: page counts are adjacent differences of indptr; a
+ * row is the sequence's pages followed by zeros; ctx = (pages - 1) *
+ * page_size + last_page_len).
+ *   page_indptr [num_seqs + 1], page_indices [page_indptr[num_seqs]],
+ *   last_page_len [num_seqs]: int32 device arrays.
+ *   block_tables [num_seqs, row_stride] int32 device array; columns
+ *                0 .. max_blocks - 1 of every row are written.
+ *   ctx_lens     [num_seqs] int32 device array, written.
+ *   bad_rows     optional [1] int32 device array, written: the number of
+ *                rows with no pages, more than max_blocks pages or
+ *                last_page_len outside 1 .. page_size; such rows are written
+ *                as all padding with ctx_lens 0, and page_indices is not read
+ *                for them.
+ * Errors: GDN_EINVAL for null pointers, num_seqs < 0, page_size <= 0,
+ * max_blocks < 0 or row_stride < max_blocks.
+ */
+int gdn_csr_to_block_table(const int32_t* page_indptr, const int32_t* page_indices,
+                           const int32_t* last_page_len, int32_t num_seqs, int32_t page_size,
+                           int32_t max_blocks, int32_t* block_tables, int64_t row_stride,
+                           int32_t* ctx_lens, int32_t* bad_rows, hipStream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* gdn_last_error(void);
 

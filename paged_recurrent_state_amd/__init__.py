@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     DecodeSlots,
     GDNError,
     PrefillSlots,
+    block_table_to_csr,
+    csr_to_block_table,
     decode,
     decode_paged,
     decode_slots,

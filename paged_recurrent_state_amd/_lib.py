@@ -60,7 +60,7 @@ class DecodeSlots(NamedTuple):
 
 EXPORTS = ["gdn_prefill_slots", "gdn_decode_slots", "gdn_prefill_workspace_size",
            "gdn_prefill_paged", "gdn_decode_paged", "gdn_prefill", "gdn_decode",
-           "gdn_last_error", "gdn_version"]
+           "gdn_block_table_to_csr", "gdn_csr_to_block_table", "gdn_last_error", "gdn_version"]
 
 
 def lib_path() -> str:
@@ -88,6 +88,8 @@ def load():
                                   I64, P, I32, P, I64, P, P, P, I32, I32, P, P, SZ, P]),
         "gdn_decode": (C.c_int, [C.POINTER(Dims), P, P, P, P, P, I32, P, I64, P, P, I64, P,
                                  I32, P, P]),
+        "gdn_block_table_to_csr": (C.c_int, [P, I64, P, I32, I32, I32, P, P, P, P, P]),
+        "gdn_csr_to_block_table": (C.c_int, [P, P, P, I32, I32, I32, P, I64, P, P, P]),
         "gdn_last_error": (C.c_char_p, []),
         "gdn_version": (C.c_char_p, []),
     }
@@ -219,6 +221,61 @@ def decode_slots(page_indices, page_indptr, last_page_len,
     _check(lib.gdn_decode_slots(_ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len), B,
                                 C.byref(sc), _stream(dev)))
     return out
+
+
+def block_table_to_csr(block_tables, ctx_lens, page_size: int, bad_rows: Optional[torch.Tensor] = None):
+    """Padded block table [B, max_blocks] int32 + ctx_lens [B] int32 -> (page_indptr,
+    page_indices, last_page_len), all on the device (two launches, no host sync).
+
+    ``page_indices`` is returned at its capacity, B * max_blocks entries; the
+    first ``page_indptr[-1]`` are the pages.  ``bad_rows`` (a [1] int32 device
+    tensor), when given, receives the number of rows the CSR form cannot hold.
+    """
+    lib = load()
+    dev = block_tables.device
+    if block_tables.dim() != 2 or block_tables.dtype != torch.int32 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be a [B, max_blocks] int32 tensor with unit column stride")
+    _need(ctx_lens, "ctx_lens", torch.int32, dev)
+    B, mb = block_tables.shape
+    if ctx_lens.shape[0] != B:
+        raise ValueError("ctx_lens must have one entry per block-table row")
+    if bad_rows is not None:
+        _need(bad_rows, "bad_rows", torch.int32, dev)
+    indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    indices = torch.empty(max(B * mb, 1), dtype=torch.int32, device=dev)
+    lpl = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    # empty tensors have no storage: stand-ins that are never read
+    table = block_tables if block_tables.numel() else indices
+    ctx = ctx_lens if B else lpl
+    _check(lib.gdn_block_table_to_csr(_ptr(table), max(block_tables.stride(0), mb), _ptr(ctx), B,
+                                      mb, int(page_size), _ptr(indptr), _ptr(indices), _ptr(lpl),
+                                      _ptr(bad_rows), _stream(dev)))
+    lpl = lpl[:B]
+    return indptr, indices, lpl
+
+
+def csr_to_block_table(page_indptr, page_indices, last_page_len, page_size: int, max_blocks: int,
+                       bad_rows: Optional[torch.Tensor] = None):
+    """CSR page table -> (block_tables [B, max_blocks] int32 padded with 0, ctx_lens [B]
+    int32), on the device (no host sync).  ``bad_rows`` as in block_table_to_csr."""
+    lib = load()
+    dev = page_indptr.device
+    for t, nm in ((page_indices, "page_indices"), (page_indptr, "page_indptr"),
+                  (last_page_len, "last_page_len")):
+        _need(t, nm, torch.int32, dev)
+    if bad_rows is not None:
+        _need(bad_rows, "bad_rows", torch.int32, dev)
+    B = last_page_len.shape[0]
+    mb = int(max_blocks)
+    table = torch.empty(max(B, 1), max(mb, 1), dtype=torch.int32, device=dev)
+    ctx = torch.empty(max(B, 1), dtype=torch.int32, device=dev)
+    # empty tensors have no storage: stand-ins that are never read
+    indices = page_indices if page_indices.numel() else ctx
+    lpl = last_page_len if B else ctx
+    _check(lib.gdn_csr_to_block_table(_ptr(page_indptr), _ptr(indices), _ptr(lpl), B,
+                                      int(page_size), mb, _ptr(table), table.stride(0), _ptr(ctx),
+                                      _ptr(bad_rows), _stream(dev)))
+    return table[:B, :mb], ctx[:B]
 
 
 def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_indptr,

@@ -197,6 +197,44 @@ int gdn_decode_slots(const int32_t* page_indices, const int32_t* page_indptr,
   return ok();
 }
 
+int gdn_block_table_to_csr(const int32_t* block_tables, int64_t row_stride,
+                           const int32_t* ctx_lens, int32_t num_seqs, int32_t max_blocks,
+                           int32_t page_size, int32_t* page_indptr, int32_t* page_indices,
+                           int32_t* last_page_len, int32_t* bad_rows, hipStream_t stream) {
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (page_size <= 0) return fail(GDN_EINVAL, "page_size must be positive (got %d)", page_size);
+  if (max_blocks < 0 || row_stride < max_blocks)
+    return fail(GDN_EINVAL, "need 0 <= max_blocks <= row_stride (got %d, %lld)", max_blocks,
+                (long long)row_stride);
+  if (!block_tables || !ctx_lens || !page_indptr || !page_indices || !last_page_len)
+    return fail(GDN_EINVAL, "block table, lengths and CSR outputs must not be NULL");
+  if (int rc = launched(launch_block_table_to_csr(block_tables, row_stride, ctx_lens, num_seqs,
+                                                  max_blocks, page_size, page_indptr,
+                                                  page_indices, last_page_len, bad_rows, stream),
+                        "block table to CSR"))
+    return rc;
+  return ok();
+}
+
+int gdn_csr_to_block_table(const int32_t* page_indptr, const int32_t* page_indices,
+                           const int32_t* last_page_len, int32_t num_seqs, int32_t page_size,
+                           int32_t max_blocks, int32_t* block_tables, int64_t row_stride,
+                           int32_t* ctx_lens, int32_t* bad_rows, hipStream_t stream) {
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (page_size <= 0) return fail(GDN_EINVAL, "page_size must be positive (got %d)", page_size);
+  if (max_blocks < 0 || row_stride < max_blocks)
+    return fail(GDN_EINVAL, "need 0 <= max_blocks <= row_stride (got %d, %lld)", max_blocks,
+                (long long)row_stride);
+  if (!page_indptr || !page_indices || !last_page_len || !block_tables || !ctx_lens)
+    return fail(GDN_EINVAL, "CSR table and block-table outputs must not be NULL");
+  if (int rc = launched(launch_csr_to_block_table(page_indptr, page_indices, last_page_len,
+                                                  num_seqs, page_size, max_blocks, block_tables,
+                                                  row_stride, ctx_lens, bad_rows, stream),
+                        "CSR to block table"))
+    return rc;
+  return ok();
+}
+
 int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const int32_t* cu_seqlens,
                       int32_t num_seqs, int64_t total_tokens, float* state_pool,

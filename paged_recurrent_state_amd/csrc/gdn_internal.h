@@ -101,6 +101,14 @@ hipError_t launch_general_slots(const int32_t* cu, int B, const void* sidx, cons
                                 const void* cstart, const void* plen, int idx64, int has_init,
                                 int write_final, int32_t* read, int32_t* write, int32_t* ckpt,
                                 int32_t* prefix, int32_t* chunk_start, hipStream_t s);
+hipError_t launch_block_table_to_csr(const int32_t* table, int64_t row_stride, const int32_t* ctx,
+                                     int B, int max_blocks, int ps, int32_t* indptr,
+                                     int32_t* indices, int32_t* lpl, int32_t* bad,
+                                     hipStream_t s);
+hipError_t launch_csr_to_block_table(const int32_t* indptr, const int32_t* indices,
+                                     const int32_t* lpl, int B, int ps, int max_blocks,
+                                     int32_t* table, int64_t row_stride, int32_t* ctx,
+                                     int32_t* bad, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 

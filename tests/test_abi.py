@@ -140,3 +140,19 @@ def test_empty_batches_are_no_ops(lib):
                                  C.c_void_p(0x1000), C.c_void_p(0x1000), 64, None, None, None,
                                  0, None) == 0
     assert lib.gdn_last_error() == b""
+
+
+def test_table_conversions_reject_bad_args(lib):
+    f = C.c_void_p(0x1000)
+    # block table -> CSR: num_seqs < 0, page_size <= 0, max_blocks > row_stride, NULL outputs
+    assert lib.gdn_block_table_to_csr(f, 8, f, -1, 4, 16, f, f, f, None, None) == -1
+    assert lib.gdn_block_table_to_csr(f, 8, f, 2, 4, 0, f, f, f, None, None) == -1
+    assert lib.gdn_block_table_to_csr(f, 3, f, 2, 4, 16, f, f, f, None, None) == -1
+    assert lib.gdn_block_table_to_csr(f, 8, f, 2, -1, 16, f, f, f, None, None) == -1
+    assert lib.gdn_block_table_to_csr(f, 8, f, 2, 4, 16, f, None, f, None, None) == -1
+    assert b"NULL" in lib.gdn_last_error()
+    # CSR -> block table: the same rules
+    assert lib.gdn_csr_to_block_table(f, f, f, -1, 16, 4, f, 8, f, None, None) == -1
+    assert lib.gdn_csr_to_block_table(f, f, f, 2, -16, 4, f, 8, f, None, None) == -1
+    assert lib.gdn_csr_to_block_table(f, f, f, 2, 16, 9, f, 8, f, None, None) == -1
+    assert lib.gdn_csr_to_block_table(f, f, None, 2, 16, 4, f, 8, f, None, None) == -1
