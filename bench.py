@@ -21,7 +21,6 @@ development; they print a line of the same form.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -63,10 +62,12 @@ COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_counters__prefill_path_and_dec
 
 
 def kernel_sources_digest() -> str:
-    """sha256 (first 16 hex digits) of the HIP sources the counters were taken
-    on, with comments and whitespace removed (comment edits keep the digest)."""
+    """sha256 (first 16 hex digits) of the sources of the measured kernels
+    (prefill path and decode) the counters were taken on, with comments and
+    whitespace removed (comment edits keep the digest)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "paged_recurrent_state_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "paged_recurrent_state_amd", "csrc")
+    for f in [os.path.join(csrc, n) for n in ("gdn_decode.hip", "gdn_internal.h", "gdn_prefill.hip")]:
         with open(f, encoding="utf-8") as fh:
             code = fh.read()
         code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
