@@ -33,8 +33,9 @@
  * by another sequence of the same call.  Breaking these is undefined
  * behaviour.
  *
- * Supported: K = V = 128, H a multiple of Hqk, page_size and
- * checkpoint_every_n_tokens positive multiples of 64.
+ * Supported: K = V = 128, H a multiple of Hqk, page_size a positive multiple
+ * of 64, any positive checkpoint_every_n_tokens (a checkpoint inside a 64-token
+ * chunk costs one more state-update product in that chunk).
  */
 #ifndef GDN_PAGED_H
 #define GDN_PAGED_H
@@ -199,8 +200,8 @@ int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const
  *   The three state buffers may be the same memory.
  * Errors: GDN_EINVAL (as above; output_state_indices without output_state or
  * output_final_state; checkpoint rows without N > 0, prefix_lens,
- * checkpoint_cu_starts or state_checkpoints), GDN_EUNSUPPORTED (N not a
- * multiple of 64, K or V != 128), GDN_EWORKSPACE, GDN_ELAUNCH.
+ * checkpoint_cu_starts or state_checkpoints), GDN_EUNSUPPORTED (K or V !=
+ * 128), GDN_EWORKSPACE, GDN_ELAUNCH.
  */
 int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const int32_t* cu_seqlens,

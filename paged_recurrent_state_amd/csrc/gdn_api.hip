@@ -364,10 +364,6 @@ int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void
       return fail(GDN_EINVAL,
                   "checkpoint_state_indices needs checkpoint_every_n_tokens > 0, prefix_lens, "
                   "checkpoint_cu_starts and state_checkpoints");
-    if (checkpoint_every_n_tokens % kChunk != 0)
-      return fail(GDN_EUNSUPPORTED,
-                  "checkpoint_every_n_tokens must be a multiple of 64 (got %d)",
-                  checkpoint_every_n_tokens);
     if (checkpoint_row_stride < blk) return fail(GDN_EINVAL, "checkpoint_row_stride < H*V*K");
   }
   if (num_seqs == 0 || total_tokens == 0) return ok();

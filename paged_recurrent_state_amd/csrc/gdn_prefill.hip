@@ -628,8 +628,8 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 
   int64_t ckpt_row = -1;  // checkpoint of the previous chunk's end, stored one iteration late
   // the next checkpoint position (the first multiple of the interval past the
-  // prefix; chunk ends are multiples of 64, and so is the interval) and its
-  // index among the call's checkpoints of this sequence
+  // prefix: the state after the token at that many tokens of the sequence)
+  // and its index among the call's checkpoints of this sequence
   int ck_next = p.ckpt_idx ? (pre / p.ckpt_every + 1) * p.ckpt_every : -1;
   int ck_j = 0;
   for (int ci = 0; ci < nch; ++ci) {
@@ -640,6 +640,11 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     const u16* Qb = sm.Qb[X];
     const u16* Tf = sm.Tf[X];
     const float(*sc)[kChunk] = sm.scal[X];
+    // position after the chunk's last row; checkpoints strictly inside the
+    // chunk (intervals that are not multiples of 64) are taken from the
+    // chunk's start state, so its decay then waits until they are done
+    const int a_end = (pre & ~(kChunk - 1)) + kChunk * (ci + 1);
+    const bool ck_inside = ck_next > 0 && ck_next < a_end && ck_next <= pre + s.L;
 
     // Memory traffic of the iteration, by wave pairs at different points so
     // that of the two waves sharing a SIMD (w and w + 4) one computes while
@@ -700,7 +705,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       }
     }
     // S's decay over the chunk (the update adds onto it at the end)
-    {
+    if (!ck_inside) {
       const float gC = sc[2][kChunk - 1];
 #pragma unroll
       for (int mk = 0; mk < 8; ++mk) accS[mk] = accS[mk] * gC;
@@ -876,6 +881,45 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
             u32x2{f2bf2(z[mt][0], z[mt][1]), f2bf2(z[mt][2], z[mt][3])};
     }
 
+    // Checkpoints after rows r inside the chunk, from the start state S:
+    // S_r = gamma_r S + (dec_r E)^T K with dec_r = exp(G_r - G_t) on rows
+    // t <= r and 0 after them (the state update truncated at row r); then the
+    // decay of S postponed above.
+    if (ck_inside) {
+      while (ck_next < a_end && ck_next <= pre + s.L) {
+        const int r = ck_next - (a_end - kChunk) - 1;
+        const int64_t row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + ck_j, p.ckpt_idx64);
+        ++ck_j;
+        ck_next += p.ckpt_every;
+        if (row < 0) continue;
+        const float Gr = sc[1][r], gr = sc[2][r];
+        f32x4 Er[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 Gt = *(const f32x4*)&sc[1][16 * mt + 4 * gq];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            Er[mt][j] = 16 * mt + 4 * gq + j <= r ? __builtin_amdgcn_exp2f(Gr - Gt[j]) * E[mt][j] : 0.f;
+        }
+        bf16x8 rh[2], rl[2];
+        split_rows(Er, 0, rh[0], rl[0]);
+        split_rows(Er, 1, rh[1], rl[1]);
+        f32x4 acc[8];
+#pragma unroll
+        for (int mk = 0; mk < 8; ++mk) acc[mk] = accS[mk] * gr;
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+          const bf16x8 kt = lds_frag(sm.Ktf, f, lane);  // k block f/2, t-step f%2
+          acc[f >> 1] = mfma16x16x32(kt, rh[f & 1], acc[f >> 1]);
+          acc[f >> 1] = mfma16x16x32(kt, rl[f & 1], acc[f >> 1]);
+        }
+        store_state(p.ckpt + row * p.ckpt_stride + head_off, acc, gq);
+      }
+      const float gC = sc[2][kChunk - 1];
+#pragma unroll
+      for (int mk = 0; mk < 8; ++mk) accS[mk] = accS[mk] * gC;
+    }
+
     // S <- gamma_last S + (dec E)^T K (the decay was applied beside Y); 4
     // groups (ks, mk/4) of 4 K^T fragments, the next group read while this
     // one multiplies (hi pass over the group's 4 blocks, then lo pass)
@@ -902,7 +946,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 
     // checkpoint at this chunk's end?
     ckpt_row = -1;
-    if ((pre & ~(kChunk - 1)) + kChunk * (ci + 1) == ck_next && ck_next <= pre + s.L) {
+    if (a_end == ck_next && ck_next <= pre + s.L) {
       ckpt_row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + ck_j, p.ckpt_idx64);
       ++ck_j;
       ck_next += p.ckpt_every;

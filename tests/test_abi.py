@@ -116,8 +116,6 @@ def test_general_prefill_companion_rules(lib):
     assert call(ck_idx=f, prefix=None) == -1
     assert call(ck_idx=f, ck_starts=None) == -1
     assert call(ck_idx=f, ckpt=None) == -1
-    # N not a multiple of 64 is valid per the page but not built here
-    assert call(ck_idx=f, N=100) == -2
     assert call(idx_dtype=7) == -1
 
 

@@ -228,14 +228,17 @@ def test_general_decode_rows(idx_dtype):
         check_state(out[r], s)
 
 
-@pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
-def test_general_prefill_checkpoints(idx_dtype):
-    """Slot-argument prefill in pieces with checkpoints every 128 tokens into a
-    separate buffer (-1 rows skipped) and a padded row stride."""
+@pytest.mark.parametrize("idx_dtype,N,g_scale", [(torch.int32, 128, 1.0), (torch.int64, 128, 1.0),
+                                                  (torch.int32, 100, 0.1), (torch.int32, 48, 1.0),
+                                                  (torch.int64, 17, 0.1), (torch.int32, 1, 0.1)])
+def test_general_prefill_checkpoints(idx_dtype, N, g_scale):
+    """Slot-argument prefill in pieces with checkpoints every N tokens into a
+    separate buffer (-1 rows skipped) and a padded row stride.  N not a
+    multiple of 64 puts checkpoints inside chunks (N = 1: after every token)."""
     m = lib()
     H = Hqk = 2
-    N = 128
-    c = workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N, num_rows=3)
+    c = workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N, num_rows=3,
+                          g_scale=g_scale)
     c = cuda(c)
     ckpt = workloads.nan_pool(1000 // N, H, 128, 128, device=DEV, row_stride=H * 128 * 128 + 64)
     slot_pool = c["pool"]
