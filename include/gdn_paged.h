@@ -127,6 +127,14 @@ int gdn_decode_slots(const int32_t* page_indices, const int32_t* page_indptr,
  * Workspace bytes gdn_prefill_paged / gdn_prefill need for a batch of
  * `total_tokens` new tokens in `num_seqs` sequences (an upper bound that
  * depends on sizes only, so it can be sized once).  0 on bad dims.
+ * Batches whose (sequence, v-head) pairs leave most of the GPU idle (B * H <=
+ * 64) and whose sequences are long run the recurrence sequence-parallel:
+ * every sequence is cut into segments, each segment's transition S -> S M +
+ * N is computed in parallel, the maps are composed in order, and the segments
+ * rerun from their true start states.  The workspace then also holds three
+ * states (H * V * K floats each) per segment.  The environment variable
+ * GDN_PREFILL_SPLIT_CHUNKS = m, read at every call (also by this function),
+ * forces segments of m chunks of 64 tokens; 0 turns the split off.
  */
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs,
                                   const gdn_dims_t* dims);

@@ -3,7 +3,9 @@
 // synchronizes with the device or allocates memory.
 #include "gdn_paged.h"
 
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -44,14 +46,44 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // fragments + scalars).
 // A sequence with L new tokens spans ceil(((prefix mod 64) + L) / 64) <=
 // (L + 126) / 64 chunks, so a batch never has more than T / 64 + 2 B of them.
+// With the sequence-parallel recurrence (split_m > 0) it also holds the
+// segment records of both passes, the per-sequence scan records and the
+// segment states (start, offset and transition of every segment: at most 3
+// per segment, rows of H * V * K floats).
 struct WsLayout {
   int64_t nc;
-  size_t slots, order, zero, tab, T, scal, total;
+  int split_m;
+  int64_t cap1, cap2, rows;
+  size_t slots, order, zero, tab, T, scal, seg1, seg2, scan, counts, states, total;
 };
+
+// Segment length (chunks) of the sequence-parallel recurrence, 0 for whole
+// sequences.  With n = B * H (sequence, v-head) pairs on the chip's 256
+// compute units, whole sequences take one round of c chunks; G segments per
+// sequence take about two rounds of c / G chunks for the first pass (2G - 2
+// runs per sequence, without outputs) and one for the second (G runs), plus
+// G - 1 scan steps.  G = 256 / n fills the second pass once, and the split
+// wins by about G / 3: only when n <= 64 and the sequences are long.
+// GDN_PREFILL_SPLIT_CHUNKS = m forces segments of m chunks (0: never split).
+int split_chunks(int64_t T, int B, int H) {
+  if (const char* f = getenv("GDN_PREFILL_SPLIT_CHUNKS")) return std::max(0, atoi(f));
+  const int64_t n = (int64_t)B * H;
+  if (B <= 0 || n > 64) return 0;
+  const int64_t nc = T / kChunk + 2 * (int64_t)B;
+  if (nc < 16 * (int64_t)B) return 0;  // short sequences: nothing to win
+  const int64_t G = 256 / n;              // segments per sequence
+  return (int)std::max<int64_t>(4, (nc + B * G - 1) / (B * G));
+}
 
 WsLayout ws_layout(int64_t T, int B, int H) {
   WsLayout w;
   w.nc = T / kChunk + 2 * (int64_t)B + 1;
+  w.split_m = split_chunks(T, B, H);
+  // a sequence of c chunks has ceil(c / m) <= c / m + 1 segments
+  const int64_t segs = w.split_m > 0 ? w.nc / w.split_m + B : 0;
+  w.cap1 = 2 * segs;
+  w.cap2 = segs;
+  w.rows = 3 * segs;
   size_t off = 0;
   w.slots = off;
   off += align256((size_t)5 * B * sizeof(int32_t));
@@ -65,6 +97,19 @@ WsLayout ws_layout(int64_t T, int B, int H) {
   off += align256((size_t)w.nc * H * kRecWords * sizeof(u16));
   w.scal = off;
   off += align256((size_t)w.nc * H * kRecScal * sizeof(float));
+  w.seg1 = w.seg2 = w.scan = w.counts = w.states = off;
+  if (w.split_m > 0) {
+    w.seg1 = off;
+    off += align256((size_t)w.cap1 * kSegWords * sizeof(int32_t));
+    w.seg2 = off;
+    off += align256((size_t)w.cap2 * kSegWords * sizeof(int32_t));
+    w.scan = off;
+    off += align256((size_t)B * 4 * sizeof(int32_t));
+    w.counts = off;
+    off += 256;
+    w.states = off;
+    off += align256((size_t)w.rows * H * kDim * kDim * sizeof(float));
+  }
   w.total = off;
   return w;
 }
@@ -143,6 +188,17 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.ckpt_idx = ckpt_idx;
   pp.ckpt_idx64 = ckpt_idx64;
   pp.ckpt_every = ckpt_every;
+  pp.split_m = L.split_m;
+  pp.seg_cap1 = (int)L.cap1;
+  pp.seg_cap2 = (int)L.cap2;
+  pp.seg1 = (int32_t*)((char*)ws + L.seg1);
+  pp.seg2 = (int32_t*)((char*)ws + L.seg2);
+  pp.seg_scan = (int4*)((char*)ws + L.scan);
+  pp.seg_counts = (int32_t*)((char*)ws + L.counts);
+  pp.ws_state = (float*)((char*)ws + L.states);
+  pp.ws_state_stride = (int64_t)d->num_v_heads * kDim * kDim;
+  pp.vseq = nullptr;
+  pp.vcount = nullptr;
   if (int rc = launched(launch_prefill(pp, L.nc, stream), "prefill kernels")) return rc;
   return ok();
 }

@@ -27,10 +27,23 @@ struct SlotsDev {
 constexpr int kFragElems = 64 * 8;  // one 16x16x32 MFMA operand fragment, bf16 elements
 
 // Per (chunk slot, v-head) record the intra-chunk kernel hands to the
-// recurrence: T = (I + A)^-1 as 8 hi + 8 lo bf16 operand fragments, and the
-// per-row scalars beta, G (log2 units), gamma = 2^G, exp(G_last - G).
+// recurrence: T diag(beta), T = (I + A)^-1, as its 6 nonzero hi and 6 lo bf16
+// operand fragments, and the per-row scalars beta, G (log2 units), gamma =
+// 2^G, exp(G_last - G).
 constexpr int kRecWords = 2 * 6 * kFragElems;  // bf16 elements (12 KiB): T's 6 nonzero fragments, hi and lo
 constexpr int kRecScal = 4 * kChunk;           // floats (1 KiB)
+
+// Sequence-parallel recurrence (long sequences in batches too small to fill
+// the chip): every sequence's chunks are cut into segments of m chunks, and
+// the recurrence runs over segment records of kSegWords int32 each
+// {first token, tokens, prefix (absolute position of the segment's start),
+// first chunk slot, read row, write row, first checkpoint index, mode}.
+// Rows: >= 0 a row of the caller's state buffers, -1 none (zero state / no
+// store), <= -2 row (-2 - r) of the workspace's segment states.
+constexpr int kSegWords = 8;
+constexpr int kSegNormal = 0;  // a real run: outputs, checkpoints, final state
+constexpr int kSegOffset = 1;  // from the zero state, no outputs: the segment's offset N
+constexpr int kSegMap = 2;     // from the identity with v = 0, no outputs: its transition M
 
 struct PrefillParams {
   const u16* q;
@@ -61,6 +74,17 @@ struct PrefillParams {
   const void* ckpt_idx;
   int ckpt_idx64;
   int ckpt_every;
+  // sequence-parallel recurrence (split_m > 0: segments of split_m chunks)
+  int split_m;
+  int seg_cap1, seg_cap2;  // segment records the two passes have room for
+  int32_t* seg1;           // [seg_cap1][kSegWords] first pass (workspace)
+  int32_t* seg2;           // [seg_cap2][kSegWords] second pass (workspace)
+  int4* seg_scan;          // [B] {segments, first workspace state row, -, -}
+  int32_t* seg_counts;     // [2] records in each pass
+  float* ws_state;         // workspace states, rows of H * V * K floats
+  int64_t ws_state_stride;
+  const int32_t* vseq;     // the records this launch walks (null: whole sequences)
+  const int32_t* vcount;   // how many of them are real
 };
 
 struct DecodeParams {
@@ -157,6 +181,37 @@ __device__ __forceinline__ bf16x8 round8(const float* x) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) h[i] = f2bf2(x[2 * i], x[2 * i + 1]);
   return as_bf16x8(h);
+}
+
+// Workgroup-wide exclusive scan of one int per thread (blockDim.x a multiple of
+// 64, at most 1024); *total receives the workgroup's sum.  Every thread must
+// call it (it synchronizes the workgroup).
+__device__ inline int block_exclusive_scan(int x, int* total) {
+  __shared__ int wsum[16];
+  __shared__ int tot;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = wsum[w];
+      wsum[w] = run;
+      run += t;
+    }
+    tot = run;
+  }
+  __syncthreads();
+  const int out = wsum[wid] + incl - x;
+  *total = tot;
+  __syncthreads();  // wsum / tot are reused by the next call
+  return out;
 }
 
 // Row index, within a 64-row operand, of slot j (0..7) of lane group gq (0..3)

@@ -537,7 +537,10 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
 }
 
 
-template <int NW>
+// OUT: the run produces outputs, checkpoints and its final state (whole
+// sequences, and the sequence-parallel second pass); without, it is a
+// first-pass segment run (offset or transition) that only ends in a state.
+template <int NW, bool OUT>
 __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   constexpr int kThreads = NW * 64;
   constexpr int kTiles = 8 / NW;  // V-tiles per head
@@ -550,22 +553,44 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 
   // Longest sequences first: blockIdx walks p.order (sorted by chunk count);
   // the V-tiles of a head sit H blocks apart (same XCD when H % 8 == 0).
+  // With p.vseq the items are segments of sequences instead (the
+  // sequence-parallel passes), each described by its own record.
   const int per_seq = p.H * kTiles;
   const int item = blockIdx.x;
-  const int b = p.order[item / per_seq];
   const int r_in = item - (item / per_seq) * per_seq;
   const int vt = r_in / p.H;
   Seq s;
   s.h = head_of(r_in - vt * p.H, p.H, p.group);
-  s.tok0 = p.cu_seqlens[b];
-  s.L = p.cu_seqlens[b + 1] - s.tok0;
+  int pre, cs0, rd, wr, ck_base, mode = kSegNormal;
+  if (p.vseq) {
+    const int vi = item / per_seq;
+    if (vi >= *p.vcount) return;  // beyond this pass's segments
+    const int32_t* d = p.vseq + kSegWords * vi;
+    s.tok0 = d[0];
+    s.L = d[1];
+    pre = d[2];
+    cs0 = d[3];
+    rd = d[4];
+    wr = d[5];
+    ck_base = d[6];
+    mode = d[7];
+  } else {
+    const int b = p.order[item / per_seq];
+    s.tok0 = p.cu_seqlens[b];
+    s.L = p.cu_seqlens[b + 1] - s.tok0;
+    pre = p.slots.prefix[b];
+    cs0 = p.slots.chunk_start[b];
+    rd = p.slots.read[b];
+    wr = p.slots.write[b];
+    ck_base = p.ckpt_idx ? p.slots.ckpt_start[b] : 0;
+  }
   if (s.L <= 0) return;  // a zero-length sequence writes nothing
   s.hq = s.h / p.group;
-  const int pre = p.slots.prefix[b];
   const int nch = chunks_of(pre, s.L);
-  const int cs0 = p.slots.chunk_start[b];
-  const int rd = p.slots.read[b];
-  const int wr = p.slots.write[b];
+  // a transition-map segment: identity start, v = 0; first-pass runs skip Q
+  // and every product that only feeds o
+  const bool vzero = !OUT && mode == kSegMap;
+  constexpr bool outs = OUT;
   const int vb = vt * NW + wid;  // this wave's 16-row block of the state
   const int vrow = 16 * vb + n16;
   const int64_t head_off = ((int64_t)s.h * kDim + vrow) * kDim;
@@ -586,14 +611,25 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 #pragma unroll 1
   for (int j = wid; j < 16; j += NW) {
     load_rows(sm.Kb[0], ksrc, qk_stride, p.zero_row, s, nbase, j, lane);
-    load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, j, lane);
-    load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, j, lane);
+    if (outs) load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, j, lane);
+    if (!vzero) load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, j, lane);
   }
+  if (vzero)
+    for (int i = tid; i < kTileWords / 8; i += kThreads) *(u32x4*)&sm.Vb[8 * i] = u32x4{0u, 0u, 0u, 0u};
   for (int part = wid; part < 2; part += NW) load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, part, lane);
 
   f32x4 accS[8];
-  if (rd >= 0 && p.init) {
+  if (vzero) {  // the identity: row vrow has its 1 at k = vrow
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accS[mb][r] = state_k(mb, gq) + r == vrow ? 1.f : 0.f;
+  } else if (rd >= 0 && p.init) {
     const float* src = p.init + (int64_t)rd * p.init_stride + head_off;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) accS[mb] = *(const f32x4*)(src + state_k(mb, gq));
+  } else if (rd <= -2) {  // a state of the sequence-parallel workspace
+    const float* src = p.ws_state + (int64_t)(-2 - rd) * p.ws_state_stride + head_off;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) accS[mb] = *(const f32x4*)(src + state_k(mb, gq));
   } else {
@@ -630,7 +666,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   // the next checkpoint position (the first multiple of the interval past the
   // prefix: the state after the token at that many tokens of the sequence)
   // and its index among the call's checkpoints of this sequence
-  int ck_next = p.ckpt_idx ? (pre / p.ckpt_every + 1) * p.ckpt_every : -1;
+  int ck_next = OUT && p.ckpt_idx ? (pre / p.ckpt_every + 1) * p.ckpt_every : -1;
   int ck_j = 0;
   for (int ci = 0; ci < nch; ++ci) {
     const int X = ci & 1;
@@ -657,7 +693,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     } else if (more) {
       // every wave loads 16 / NW consecutive blocks of the next K and Q
       load_tile<16 / NW>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
-      load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+      if (outs) load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
     if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
 
@@ -713,16 +749,16 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 
     if constexpr (NW == 8) {
       if (wid == 2 || wid == 3) {
-        if (ci > 0) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
+        if (ci > 0 && OUT) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
       } else if (more && wid >= 4) {
         if (wid < 6) {
-          load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
+          if (outs) load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
         } else {
           load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid - 6, lane);
         }
       }
     } else {
-      if (ci > 0) write_o_tile<NW>(p, sm, s, n0 - kChunk, 16 * NW * vt, tid);
+      if (ci > 0 && OUT) write_o_tile<NW>(p, sm, s, n0 - kChunk, 16 * NW * vt, tid);
       if (more) {
         for (int part = wid; part < 2; part += NW)
           load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, part, lane);
@@ -740,7 +776,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         z[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        qf[0][mt] = tile_frag(Qb, mt * 4, lane);
+        if (outs) qf[0][mt] = tile_frag(Qb, mt * 4, lane);
       }
       f32x4 R[4];
 #pragma unroll
@@ -750,16 +786,18 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
         for (int r = 0; r < 4; ++r) R[mt][r] = -gm[r] * y[mt][r];
         R[mt] = mfma16x16x32(vf[mt], vsel, R[mt]);
       }
+      if (outs) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < 3) {
+        for (int ks = 0; ks < 4; ++ks) {
+          if (ks < 3) {
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) qf[(ks + 1) & 1][mt] = tile_frag(Qb, mt * 4 + ks + 1, lane);
+            for (int mt = 0; mt < 4; ++mt) qf[(ks + 1) & 1][mt] = tile_frag(Qb, mt * 4 + ks + 1, lane);
+          }
+          sched_fence();
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Shi[ks], qf[ks & 1][mt], z[mt]);
+          sched_fence();
         }
-        sched_fence();
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) z[mt] = mfma16x16x32(Shi[ks], qf[ks & 1][mt], z[mt]);
-        sched_fence();
       }
       split_rows(R, 0, Rhi[0], Rlo[0]);
       split_rows(R, 1, Rhi[1], Rlo[1]);
@@ -804,7 +842,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 #pragma unroll
     for (int bi = 0; bi < (NW == 8 ? 2 : (10 + NW - 1) / NW); ++bi) {
       const int blk = NW == 8 ? (bi == 0 ? wid : (wid == 2 || wid == 3 ? wid + 6 : 10)) : wid + NW * bi;
-      if (blk >= 10) break;
+      if (blk >= 10 || !outs) break;
       const int bt = tri_i(blk), bs = tri_j(blk);
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
@@ -857,15 +895,15 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
     if constexpr (NW == 8) {
-      if (more && wid < 4) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * wid, lane);
-    } else if (more) {
+      if (more && wid < 4 && !vzero) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * wid, lane);
+    } else if (more && !vzero) {
       load_tile<16 / NW>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
 
     // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
     // state fragments and E act as A operands, Q and P fragments as B, so a
     // lane ends up with 4 adjacent v of one token (one 8-byte LDS store)
-    {
+    if (outs) {
       bf16x8 pfr[6];
       // P fragments (mt, ks) with mt >= 2 or ks == 0: 0, 2, 4, 5, 6, 7
 #pragma unroll
@@ -888,7 +926,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     if (ck_inside) {
       while (ck_next < a_end && ck_next <= pre + s.L) {
         const int r = ck_next - (a_end - kChunk) - 1;
-        const int64_t row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + ck_j, p.ckpt_idx64);
+        const int64_t row = ld_index(p.ckpt_idx, ck_base + ck_j, p.ckpt_idx64);
         ++ck_j;
         ck_next += p.ckpt_every;
         if (row < 0) continue;
@@ -947,17 +985,20 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     // checkpoint at this chunk's end?
     ckpt_row = -1;
     if (a_end == ck_next && ck_next <= pre + s.L) {
-      ckpt_row = ld_index(p.ckpt_idx, p.slots.ckpt_start[b] + ck_j, p.ckpt_idx64);
+      ckpt_row = ld_index(p.ckpt_idx, ck_base + ck_j, p.ckpt_idx64);
       ++ck_j;
       ck_next += p.ckpt_every;
     }
     wait_loads();     // the next chunk's tiles have landed (this wave's part)
     __syncthreads();  // ... and every wave's; this chunk's LDS operands are free
   }
-  if constexpr (NW == 8) write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
-  else write_o_tile<NW>(p, sm, s, nbase + kChunk * (nch - 1), 16 * NW * vt, tid);
+  if constexpr (OUT) {
+    if constexpr (NW == 8) write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
+    else write_o_tile<NW>(p, sm, s, nbase + kChunk * (nch - 1), 16 * NW * vt, tid);
+  }
   if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
   if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
+  if (wr <= -2) store_state(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, accS, gq);
 }
 
 // Launch plan, one workgroup: the longest-first order of the sequences (by
@@ -988,24 +1029,163 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Sequence-parallel plan, one workgroup.  Sequence b (G = ceil(chunks / m)
+// segments of m chunks; segment g starts at new token lo_g, an absolute
+// multiple of 64 for g >= 1) gets:
+//   first pass:  for g = 0 .. G-2 the segment from the zero state (its offset
+//                N_g) and from the identity with v = 0 (its transition M_g),
+//                so that S_end = S_start M_g + N_g;
+//   scan:        start_0 = the sequence's initial state, start_{g+1} =
+//                start_g M_g + N_g, g = 0 .. G-2;
+//   second pass: segments 0 .. G-1 for real from start_g (start_0: the read
+//                row), the last one writing the final state.
+// Workspace state rows of b, from row0: start_1 .. start_{G-1}, then
+// N_0 .. N_{G-2}, then M_0 .. M_{G-2}.
+__global__ __launch_bounds__(1024) void split_plan_kernel(const PrefillParams p) {
+  const int m = p.split_m, B = p.num_seqs;
+  int carry1 = 0, carry2 = 0, carry_row = 0;
+  for (int base = 0; base < B; base += blockDim.x) {
+    const int b = base + (int)threadIdx.x;
+    int L = 0, pre = 0, G = 0;
+    if (b < B) {
+      L = p.cu_seqlens[b + 1] - p.cu_seqlens[b];
+      pre = p.slots.prefix[b];
+      G = L > 0 ? (chunks_of(pre, L) + m - 1) / m : 0;
+    }
+    const int n1 = G > 1 ? 2 * (G - 1) : 0, n2 = G, nrow = G > 1 ? 3 * (G - 1) : 0;
+    int t1, t2, trow;
+    const int o1 = carry1 + block_exclusive_scan(n1, &t1);
+    const int o2 = carry2 + block_exclusive_scan(n2, &t2);
+    const int row0 = carry_row + block_exclusive_scan(nrow, &trow);
+    if (b < B) {
+      p.seg_scan[b] = int4{G, row0, 0, 0};
+      const int tok0 = p.cu_seqlens[b], cs = p.slots.chunk_start[b];
+      const int rd = p.slots.read[b], wr = p.slots.write[b];
+      const int ckb = p.ckpt_idx ? p.slots.ckpt_start[b] : 0;
+      const int nbase = (pre & ~(kChunk - 1)) - pre;
+      auto lo = [&](int g) { return g == 0 ? 0 : nbase + kChunk * m * g; };
+      auto hi = [&](int g) { return min(L, nbase + kChunk * m * (g + 1)); };
+      auto put = [](int32_t* d, int a, int b_, int c, int e, int f, int g_, int h, int i) {
+        d[0] = a; d[1] = b_; d[2] = c; d[3] = e; d[4] = f; d[5] = g_; d[6] = h; d[7] = i;
+      };
+      for (int g = 0; g <= G - 2; ++g) {
+        const int a = lo(g), n = hi(g) - a;
+        put(p.seg1 + kSegWords * (o1 + 2 * g), tok0 + a, n, pre + a, cs + g * m, -1,
+            -2 - (row0 + G - 1 + g), 0, kSegOffset);
+        put(p.seg1 + kSegWords * (o1 + 2 * g + 1), tok0 + a, n, pre + a, cs + g * m, -1,
+            -2 - (row0 + 2 * (G - 1) + g), 0, kSegMap);
+      }
+      for (int g = 0; g <= G - 1; ++g) {
+        const int a = lo(g), n = hi(g) - a;
+        const int ck = p.ckpt_idx ? ckb + (pre + a) / p.ckpt_every - pre / p.ckpt_every : 0;
+        put(p.seg2 + kSegWords * (o2 + g), tok0 + a, n, pre + a, cs + g * m,
+            g == 0 ? rd : -2 - (row0 + g - 1), g == G - 1 ? wr : -1, ck, kSegNormal);
+      }
+    }
+    carry1 += t1;
+    carry2 += t2;
+    carry_row += trow;
+  }
+  if (threadIdx.x == 0) {
+    p.seg_counts[0] = carry1;
+    p.seg_counts[1] = carry2;
+  }
+}
+
+// start_{g+1} = start_g M_g + N_g for g = 0 .. G-2, fp32, 16 state rows of
+// one (sequence, v-head) per workgroup: rows of a state evolve independently,
+// so the 8 row blocks of a head run in parallel.  The transitions M_g (64 KiB
+// each) stream into LDS straight from global memory, double-buffered (the
+// next one lands while this one multiplies); the current rows stay in LDS.
+// Thread (r, c) owns row r and the columns 4c .. 4c+3 and 64+4c .. 64+4c+3,
+// so a 16-lane group's 16-byte reads of an M row cover all 64 banks.
+struct ScanSmem {
+  float M[2][kDim][kDim];
+  float S[16][kDim];
+};
+
+__global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
+  const int rb = blockIdx.x & 7, bh = blockIdx.x >> 3;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int4 sc = p.seg_scan[b];
+  const int G = sc.x, row0 = sc.y;
+  if (G < 2) return;  // a whole sequence: nothing to compose
+  const int rd = p.slots.read[b];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = tid >> 4, c0 = 4 * (tid & 15);
+  const int64_t hoff = (int64_t)h * kDim * kDim;
+  auto state = [&](int row) { return p.ws_state + (int64_t)row * p.ws_state_stride + hoff; };
+  // M_g into buffer X: 64 blocks of 1 KiB (2 rows each), 16 per wave
+  auto fetch = [&](int g, int X) {
+    const char* src = uniform_ptr(state(row0 + 2 * (G - 1) + g));
+    const uint32_t dst = lds_addr(&sm.M[X][0][0]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int blk = 16 * wid + i;
+      lds_load16_at(dst + blk * 1024, src + blk * 1024, lane * 16);
+    }
+  };
+  fetch(0, 0);
+  // start_0: the sequence's initial state (a row of the caller's buffer or zero)
+  f32x4 i0 = {0.f, 0.f, 0.f, 0.f}, i1 = i0;
+  if (rd >= 0 && p.init) {
+    const float* s0 = p.init + (int64_t)rd * p.init_stride + hoff + (int64_t)(16 * rb + r) * kDim;
+    i0 = *(const f32x4*)(s0 + c0);
+    i1 = *(const f32x4*)(s0 + 64 + c0);
+  }
+  *(f32x4*)&sm.S[r][c0] = i0;
+  *(f32x4*)&sm.S[r][64 + c0] = i1;
+  wait_loads();
+  __syncthreads();
+  for (int g = 0; g <= G - 2; ++g) {
+    const int X = g & 1;
+    if (g + 1 <= G - 2) fetch(g + 1, X ^ 1);
+    const float* Ng = state(row0 + G - 1 + g) + (int64_t)(16 * rb + r) * kDim;
+    f32x4 a0 = *(const f32x4*)(Ng + c0), a1 = *(const f32x4*)(Ng + 64 + c0);
+#pragma unroll 8
+    for (int i = 0; i < kDim; ++i) {
+      const float sv = sm.S[r][i];
+      const f32x4 m0 = *(const f32x4*)&sm.M[X][i][c0];
+      const f32x4 m1 = *(const f32x4*)&sm.M[X][i][64 + c0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0[e] = fmaf(sv, m0[e], a0[e]);
+        a1[e] = fmaf(sv, m1[e], a1[e]);
+      }
+    }
+    float* out = state(row0 + g) + (int64_t)(16 * rb + r) * kDim;  // start_{g+1}
+    *(f32x4*)(out + c0) = a0;
+    *(f32x4*)(out + 64 + c0) = a1;
+    __syncthreads();  // every thread is done reading S and M[X]
+    *(f32x4*)&sm.S[r][c0] = a0;
+    *(f32x4*)&sm.S[r][64 + c0] = a1;
+    wait_loads();     // this wave's part of the next M has landed
+    __syncthreads();  // ... and every wave's; the new rows are in place
+  }
+}
+
 }  // namespace
 
-template <int NW>
+template <int NW, bool OUT>
 hipError_t launch_rec(const PrefillParams& p, int64_t blocks, hipStream_t s) {
   static bool attr_set = false;  // raised once per process and instance; idempotent if raced
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)rec_kernel<NW>,
+    const hipError_t e = hipFuncSetAttribute((const void*)rec_kernel<NW, OUT>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RecSmem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  rec_kernel<NW><<<(unsigned)blocks, NW * 64, sizeof(RecSmem), s>>>(p);
+  rec_kernel<NW, OUT><<<(unsigned)blocks, NW * 64, sizeof(RecSmem), s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
+  if (p.split_m > 0 && (p.seg_cap1 <= 0 || p.seg_cap2 <= 0)) return hipErrorInvalidValue;
   plan_kernel<<<1, 1024, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs,
                                  p.num_chunk_slots, p.order, p.chunk_tab, (uint32_t*)p.zero_row);
   hipError_t e = hipGetLastError();
@@ -1024,14 +1204,41 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
     const int v = atoi(f);
     if (v == 1 || v == 2 || v == 4 || v == 8) nw = v;
   }
-  switch (nw) {
-    case 8: e = launch_rec<8>(p, blocks, s); break;
-    case 4: e = launch_rec<4>(p, blocks * 2, s); break;
-    case 2: e = launch_rec<2>(p, blocks * 4, s); break;
-    default: e = launch_rec<1>(p, blocks * 8, s); break;
+  auto rec = [&](const PrefillParams& q, int64_t items, bool out) {
+    switch (nw * 2 + out) {
+      case 17: return launch_rec<8, true>(q, items * p.H, s);
+      case 16: return launch_rec<8, false>(q, items * p.H, s);
+      case 9: return launch_rec<4, true>(q, items * p.H * 2, s);
+      case 8: return launch_rec<4, false>(q, items * p.H * 2, s);
+      case 5: return launch_rec<2, true>(q, items * p.H * 4, s);
+      case 4: return launch_rec<2, false>(q, items * p.H * 4, s);
+      case 3: return launch_rec<1, true>(q, items * p.H * 8, s);
+      default: return launch_rec<1, false>(q, items * p.H * 8, s);
+    }
+  };
+  if (p.split_m <= 0) return rec(p, p.num_seqs, true);
+  // sequence-parallel: plan, first pass, scan of the segment maps, second pass
+  split_plan_kernel<<<1, 1024, 0, s>>>(p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  PrefillParams p1 = p;
+  p1.vseq = p.seg1;
+  p1.vcount = p.seg_counts;
+  if ((e = rec(p1, p.seg_cap1, false)) != hipSuccess) return e;
+  {
+    static bool attr_set = false;  // raised once per process; idempotent if raced
+    if (!attr_set) {
+      if ((e = hipFuncSetAttribute((const void*)seg_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)sizeof(ScanSmem))) != hipSuccess)
+        return e;
+      attr_set = true;
+    }
   }
-  if (e != hipSuccess) return e;
-  return hipGetLastError();
+  seg_scan_kernel<<<(unsigned)((int64_t)p.num_seqs * p.H * 8), 256, sizeof(ScanSmem), s>>>(p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  PrefillParams p2 = p;
+  p2.vseq = p.seg2;
+  p2.vcount = p.seg_counts + 1;
+  return rec(p2, p.seg_cap2, true);
 }
 
 }  // namespace gdn

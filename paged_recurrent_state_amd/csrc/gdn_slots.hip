@@ -25,35 +25,6 @@ __device__ __forceinline__ int chunks_of(int p, int L) {
   return L > 0 ? ((p & (kChunk - 1)) + L + kChunk - 1) / kChunk : 0;
 }
 
-// Block-wide exclusive scan of one int per thread; also returns the block total.
-__device__ int block_exclusive_scan(int x, int* total) {
-  __shared__ int wsum[kScanThreads / 64];
-  __shared__ int tot;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int t = wsum[w];
-      wsum[w] = run;
-      run += t;
-    }
-    tot = run;
-  }
-  __syncthreads();
-  const int out = wsum[wid] + incl - x;
-  *total = tot;
-  __syncthreads();  // wsum / tot are reused by the next call
-  return out;
-}
-
 __global__ __launch_bounds__(kScanThreads) void prefill_slots_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ lpl, int B, int ps,

@@ -22,35 +22,6 @@ namespace {
 
 constexpr int kTabThreads = 1024;
 
-// Block-wide exclusive scan of one int per thread; returns the block total.
-__device__ int tab_exclusive_scan(int x, int* total) {
-  __shared__ int wsum[kTabThreads / 64];
-  __shared__ int tot;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int t = wsum[w];
-      wsum[w] = run;
-      run += t;
-    }
-    tot = run;
-  }
-  __syncthreads();
-  const int out = wsum[wid] + incl - x;
-  *total = tot;
-  __syncthreads();  // wsum / tot are reused by the next call
-  return out;
-}
-
 // Pages of a sequence of ctx tokens, 0 when the table cannot hold it.
 __device__ __forceinline__ int pages_of(int ctx, int ps, int max_blocks) {
   if (ctx < 1) return 0;
@@ -74,8 +45,8 @@ __global__ __launch_bounds__(kTabThreads) void csr_plan_kernel(
       lpl[b] = n ? c - (n - 1) * ps : 0;
     }
     int tot, tbad;
-    const int ex = tab_exclusive_scan(n, &tot);
-    tab_exclusive_scan(invalid, &tbad);
+    const int ex = block_exclusive_scan(n, &tot);
+    block_exclusive_scan(invalid, &tbad);
     if (b < B) indptr[b + 1] = carry + ex + n;
     carry += tot;
     nbad += tbad;
@@ -123,7 +94,7 @@ __global__ __launch_bounds__(kTabThreads) void table_bad_kernel(const int32_t* _
       invalid = !(n >= 1 && n <= max_blocks && last >= 1 && last <= ps);
     }
     int t;
-    tab_exclusive_scan(invalid, &t);
+    block_exclusive_scan(invalid, &t);
     nbad += t;
   }
   if (threadIdx.x == 0) *bad = nbad;

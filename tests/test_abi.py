@@ -48,7 +48,8 @@ def dims(H=4, Hqk=2, K=128, V=128, scale=0.0):
     return _lib.Dims(Hqk, H, K, V, scale)
 
 
-def test_workspace_size(lib):
+def test_workspace_size(lib, monkeypatch):
+    monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")  # whole-sequence recurrence
     d = dims()
     a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
     b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
@@ -63,6 +64,31 @@ def test_workspace_size(lib):
     assert b - a == 100 * 4 * (12288 + 1024) + al(103 * 16) - al(3 * 16)
     bad = dims(K=64)
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
+
+
+def test_workspace_size_sequence_parallel(lib, monkeypatch):
+    """Splitting into segments of m chunks adds the records of both passes, the
+    per-sequence scan records and up to 3 segment states per segment, with
+    ceil(c / m) <= (T/64 + 2B + 1) / m + B segments in all."""
+    d = dims()  # H = 4: one sequence leaves the chip idle, so the default splits
+    monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")
+    whole = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
+    al = lambda x: (x + 255) // 256 * 256
+    for m in (4, 7):
+        monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", str(m))
+        segs = 103 // m + 1
+        extra = al(2 * segs * 32) + al(segs * 32) + al(16) + 256 + 3 * segs * 4 * 128 * 128 * 4
+        assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == extra
+    monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS")
+    # default: ~512 / H segments in all, at least 4 chunks each -> m = 4 here
+    assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == \
+        al(52 * 32) + al(26 * 32) + al(16) + 256 + 78 * 4 * 128 * 128 * 4
+    # enough (sequence, head) pairs to fill the chip: no split
+    big = dims(H=32, Hqk=32)
+    monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")
+    w0 = lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big))
+    monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS")
+    assert lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big)) == w0
 
 
 def _prefill_paged(lib, d, page_size=128, stride=4 * 128 * 128, ws=1 << 30, pool=1, cu=1,

@@ -365,3 +365,60 @@ def test_prefill_every_tile_width(waves):
         print(f"{waves} waves per workgroup: worst paged state rel {err:.2e}")
     finally:
         del os.environ["GDN_PREFILL_TILE_WAVES"]
+
+
+@pytest.mark.parametrize("m,waves", [(1, 8), (2, 8), (3, 8), (5, 8), (2, 4)])
+def test_prefill_sequence_parallel(m, waves):
+    """The sequence-parallel recurrence forced with segments of m chunks:
+    segment 0 for real, the middle segments' offsets (zero start) and
+    transitions (identity start, v = 0), the scan of the segment maps and the
+    second pass from the scanned starts.  Ragged paged sequences with GQA and
+    slow decay (so start states matter across segments), then a sliced long
+    sequence through the general call with checkpoints inside and at the ends
+    of chunks."""
+    os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = str(m)
+    os.environ["GDN_PREFILL_TILE_WAVES"] = str(waves)
+    try:
+        pre, pool = make_case([0, 37, 128, 1000], [700, 1, 64, 900], ps=128, H=4, Hqk=2,
+                              seed=11 + m, g_scale=0.1)
+        _, _, err = check_paged_prefill(pre, pool)
+        mod = lib()
+        H = 2
+        for N in (100, 128):
+            c = cuda(workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N,
+                                       num_rows=3, g_scale=0.1))
+            ckpt = workloads.nan_pool(1000 // N, H, 128, 128, device=DEV)
+            ref_slot = np.zeros((3, H, 128, 128))
+            ref_ck = {}
+            for call in c["calls"]:
+                o = mod.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
+                                call["cu_seqlens"], initial_state=c["pool"],
+                                state_indices=call["state_indices"], output_state=c["pool"],
+                                output_state_indices=call["output_state_indices"],
+                                output_final_state=True, state_checkpoints=ckpt,
+                                checkpoint_state_indices=c["checkpoint_state_indices"],
+                                checkpoint_cu_starts=call["checkpoint_cu_starts"],
+                                prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=N)
+                torch.cuda.synchronize()
+                res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(),
+                                   call["g"].cpu(), call["beta"].cpu(), call["cu_seqlens"].cpu(),
+                                   initial_state=ref_slot,
+                                   state_indices=call["state_indices"].tolist(),
+                                   output_final_state=True,
+                                   output_state_indices=call["output_state_indices"].tolist(),
+                                   checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
+                                   checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
+                                   prefix_lens=call["prefix_lens"].tolist(),
+                                   checkpoint_every_n_tokens=N, shared_pool=False)
+                check_outputs(o, res.o)
+                ref_slot = ogdn.apply_writes(ref_slot, res.final)
+                ref_ck.update(res.checkpoints)
+                check_state(c["pool"][c["slot"]], ref_slot[c["slot"]], "slot")
+            got = [r for r in range(1000 // N) if torch.isfinite(ckpt[r]).all()]
+            assert got == sorted(ref_ck)
+            for r, st in ref_ck.items():
+                check_state(ckpt[r], st, f"checkpoint {r}")
+        print(f"segments of {m} chunks, {waves} waves: worst paged state rel {err:.2e}")
+    finally:
+        os.environ.pop("GDN_PREFILL_SPLIT_CHUNKS", None)
+        os.environ.pop("GDN_PREFILL_TILE_WAVES", None)
