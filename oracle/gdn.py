@@ -29,6 +29,15 @@ Row semantics (flashinfer.gdn_paged, "Slot arguments of chunk_gated_delta_rule")
 No chunking, no padding, no blocking: one token at a time, all heads of the
 token at once in fp64.  Inputs are upcast exactly (bf16 and fp32 values are
 representable in fp64).
+
+State dtype.  The first page asks only that a pool used by both entry points
+hold "a state dtype both support".  Reading: every state buffer of a call has
+one element type, fp32 or bf16; the arithmetic is unchanged, and a state is
+rounded to the buffer's type only where it is stored (checkpoints and the
+final state), to nearest with ties to even.  ``state_dtype="bf16"`` applies
+that rounding to the stored states (the fp64 value goes through fp32 first,
+both steps to nearest even); ``"fp32"`` keeps the fp64 states unrounded, the
+reference the fp32 path is compared against within tolerance.
 """
 
 from __future__ import annotations
@@ -90,6 +99,24 @@ def gdn_token(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return S, o
 
 
+def round_bf16(x) -> np.ndarray:
+    """fp64 values rounded to bfloat16 (via fp32, each step to nearest, ties to
+    even), returned as fp64.  bf16 keeps the upper 16 bits of an fp32: add half
+    an ulp of the kept part (0x7fff, plus 1 when the kept part is odd) and cut."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    bits = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _store(S: np.ndarray, state_dtype: str) -> np.ndarray:
+    if state_dtype == "fp32":
+        return S.copy()
+    if state_dtype == "bf16":
+        return round_bf16(S)
+    raise ValueError(f"state_dtype must be 'fp32' or 'bf16', got {state_dtype!r}")
+
+
 def _head_map(H: int, Hqk: int) -> np.ndarray:
     if H % Hqk != 0:
         raise ValueError("v-heads must be a multiple of q/k heads")
@@ -123,7 +150,8 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
             output_final_state: bool = False, output_state_indices=None,
             checkpoint_state_indices=None, checkpoint_cu_starts=None,
             prefix_lens=None, checkpoint_every_n_tokens: int = 0,
-            scale: Optional[float] = None, shared_pool: bool = True) -> Result:
+            scale: Optional[float] = None, shared_pool: bool = True,
+            state_dtype: str = "fp32") -> Result:
     """General slot-argument prefill over a packed variable-length batch.
 
     q, k: [T, Hqk, K]; v: [T, H, V]; g, beta: [T, H] or None;
@@ -133,7 +161,9 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
     ``initial_state``; without ``output_state_indices`` it writes back to its
     read row (an in-place slot update).  ``shared_pool`` says whether the
     three state buffers are one memory (for the cross-sequence hazard check).
+    ``state_dtype`` is the element type of the state buffers (module docstring).
     """
+    _store(np.zeros(1), state_dtype)  # validates the name
     q, k, v = _f64(_to_numpy(q)), _f64(_to_numpy(k)), _f64(_to_numpy(v))
     T, Hqk, K = q.shape
     H, V = v.shape[1], v.shape[2]
@@ -181,7 +211,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
                 j = (p + n) // N - p // N - 1
                 row = cidx[cstart[b] + j]
                 if row != -1:
-                    res.checkpoints[row] = S.copy()
+                    res.checkpoints[row] = _store(S, state_dtype)
                     ckpt_w.setdefault(b, set()).add(row)
         if output_final_state:
             if oidx is not None:
@@ -189,7 +219,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
             else:
                 wr = sidx[b] if sidx is not None else b
             if wr != -1:
-                res.final[wr] = S.copy()
+                res.final[wr] = _store(S, state_dtype)
                 final_w.setdefault(b, set()).add(wr)
     _check_hazards(reads, final_w, ckpt_w, shared_pool)
     return res
@@ -197,7 +227,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *,
 
 def decode(q, k, v, g, beta, *, initial_state, initial_state_indices=None,
            output_state_indices=None, scale: Optional[float] = None,
-           shared_pool: bool = True) -> Result:
+           shared_pool: bool = True, state_dtype: str = "fp32") -> Result:
     """One token per sequence.  q, k: [B, Hqk, K]; v: [B, H, V]; g, beta: [B, H].
 
     Rows default to ``b``; the write row defaults to the read row.  A read row
@@ -210,11 +240,13 @@ def decode(q, k, v, g, beta, *, initial_state, initial_state_indices=None,
     widx = ridx if output_state_indices is None else output_state_indices
     return prefill(q, k, v, g, beta, cu, initial_state=initial_state,
                    state_indices=ridx, output_final_state=True,
-                   output_state_indices=widx, scale=scale, shared_pool=shared_pool)
+                   output_state_indices=widx, scale=scale, shared_pool=shared_pool,
+                   state_dtype=state_dtype)
 
 
 def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_indptr,
-                  last_page_len, page_size: int, scale: Optional[float] = None):
+                  last_page_len, page_size: int, scale: Optional[float] = None,
+                  state_dtype: str = "fp32"):
     """Paged prefill = the slot-argument prefill with all three buffers set to
     the pool, rows from ``slots.prefill_slots``, checkpoints every ``page_size``
     tokens into ``page_indices`` (flashinfer.gdn_paged calls the paged entry
@@ -235,12 +267,12 @@ def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_i
                   checkpoint_state_indices=pidx,
                   checkpoint_cu_starts=sl["checkpoint_cu_starts"],
                   prefix_lens=sl["prefix_lens"], checkpoint_every_n_tokens=page_size,
-                  scale=scale)
+                  scale=scale, state_dtype=state_dtype)
     return res.o, res.writes(), sl
 
 
 def decode_paged(q, k, v, g, beta, state_pool, page_indices, page_indptr, last_page_len,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, state_dtype: str = "fp32"):
     """Paged decode (T = 1): rows from ``slots.decode_slots``.
 
     Returns (o, writes, slots)."""
@@ -250,7 +282,8 @@ def decode_paged(q, k, v, g, beta, state_pool, page_indices, page_indptr, last_p
     sl = _slots.decode_slots(pidx, ptr, lpl)
     res = decode(q, k, v, g, beta, initial_state=state_pool,
                  initial_state_indices=sl["initial_state_indices"],
-                 output_state_indices=sl["output_state_indices"], scale=scale)
+                 output_state_indices=sl["output_state_indices"], scale=scale,
+                 state_dtype=state_dtype)
     return res.o, res.writes(), sl
 
 

@@ -175,3 +175,52 @@ def test_gqa_head_mapping_head_by_head():
                           state_indices=[0], output_state_indices=[0])
         assert np.array_equal(res.final[0][h], one.final[0][0])
         assert np.array_equal(res.o[:, h], one.o[:, 0])
+
+
+# ---- bf16 state buffers: stored states rounded to bf16, arithmetic unchanged
+
+def test_round_bf16_matches_torch_and_ties_to_even():
+    import torch
+    rng = np.random.default_rng(20)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -3.5, 65504.0, 1e-40]])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(gdn.round_bf16(x), want)
+    # exact ties between two bf16 values go to the even one (8-bit mantissa)
+    u = 2.0 ** -7
+    assert gdn.round_bf16(1 + u / 2) == 1.0            # tie: 1.0 (even) not 1 + u
+    assert gdn.round_bf16(1 + 3 * u / 2) == 1 + 2 * u  # tie: 1 + 2u (even) not 1 + u
+    assert gdn.round_bf16(1 + u / 2 + 2.0 ** -20) == 1 + u  # just above the tie
+
+
+def test_bf16_states_identity_update_keeps_the_row():
+    # g = 0, beta = 0: the state passes through unchanged, so a bf16 row read
+    # from the pool is stored back bit for bit
+    rng = np.random.default_rng(21)
+    T, H, K, V = 5, 2, 16, 16
+    q, k, v, _, _ = rand_inputs(rng, T, H, K, V)
+    S0 = gdn.round_bf16(rng.standard_normal((1, H, V, K)))
+    res = gdn.prefill(q, k, v, np.zeros((T, H)), np.zeros((T, H)), [0, T], initial_state=S0,
+                      state_indices=[0], output_final_state=True, output_state_indices=[0],
+                      state_dtype="bf16")
+    assert np.array_equal(res.final[0], S0[0])
+
+
+def test_bf16_states_rounded_only_where_stored():
+    # one token, g = 0, beta = 1, unit key e_i: column i of the new state is v
+    # (delta rule), stored to within half a bf16 ulp; the output uses the
+    # unrounded state, so it matches the fp32-buffer run exactly
+    rng = np.random.default_rng(22)
+    H, K, V = 2, 8, 8
+    S0 = gdn.round_bf16(rng.standard_normal((1, H, V, K)))
+    k = np.zeros((1, H, K)); k[0, :, 3] = 1.0
+    q = rng.standard_normal((1, H, K)); v = rng.standard_normal((1, H, V))
+    kw = dict(initial_state=S0, state_indices=[0], output_final_state=True, output_state_indices=[0])
+    r16 = gdn.prefill(q, k, v, np.zeros((1, H)), np.ones((1, H)), [0, 1], state_dtype="bf16", **kw)
+    r32 = gdn.prefill(q, k, v, np.zeros((1, H)), np.ones((1, H)), [0, 1], **kw)
+    assert np.array_equal(r16.o, r32.o)
+    col = r16.final[0][:, :, 3]
+    assert (np.abs(col - v[0]) <= 2.0 ** -8 * np.abs(v[0]) * (1 + 1e-6)).all()  # half an ulp
+    assert np.array_equal(r16.final[0], gdn.round_bf16(r32.final[0]))
+    with pytest.raises(ValueError):
+        gdn.prefill(q, k, v, None, None, [0, 1], state_dtype="fp16", **kw)
