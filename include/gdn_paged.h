@@ -17,8 +17,13 @@
  *   v            [T, H, V]    bf16
  *   g, beta      [T, H]       fp32 (either may be NULL: g = 0, beta = 1)
  *   o            [T, H, V]    bf16, written for every new token
- *   state pools  [rows, H, V, K] fp32; each row is one dense [H, V, K] block and
- *                consecutive rows sit `row_stride` floats apart (>= H*V*K).
+ *   state pools  [rows, H, V, K] fp32 or bf16 (gdn_dims_t.state_dtype, one type
+ *                for every state buffer of a call); each row is one dense
+ *                [H, V, K] block and consecutive rows sit `row_stride`
+ *                elements apart (>= H*V*K).  The arithmetic is the same for
+ *                both types; a bf16 buffer receives each stored state rounded
+ *                to nearest even (the page asks for "a state dtype both entry
+ *                points support"; fp32 and bf16 both are).
  * Decode uses B (one token per sequence) in place of T.
  * v-head h reads q/k head h / (H / Hqk).
  *
@@ -57,6 +62,7 @@ enum {
 };
 
 enum { GDN_INDEX_INT32 = 0, GDN_INDEX_INT64 = 1 };
+enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 };
 
 /* Head geometry shared by every call. */
 typedef struct {
@@ -65,6 +71,7 @@ typedef struct {
   int32_t head_dim_k;   /* K, must be 128 */
   int32_t head_dim_v;   /* V, must be 128 */
   float scale;          /* output scale; <= 0 selects 1/sqrt(K) */
+  int32_t state_dtype;  /* GDN_STATE_F32 or GDN_STATE_BF16: element type of the state buffers */
 } gdn_dims_t;
 
 /*
@@ -163,7 +170,7 @@ size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs,
  */
 int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const int32_t* cu_seqlens,
-                      int32_t num_seqs, int64_t total_tokens, float* state_pool,
+                      int32_t num_seqs, int64_t total_tokens, void* state_pool,
                       int64_t pool_row_stride, const int32_t* page_indices,
                       const int32_t* page_indptr, const int32_t* last_page_len,
                       int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
@@ -180,7 +187,7 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
  * Errors as gdn_prefill_paged (no workspace is needed).
  */
 int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
-                     const float* g, const float* beta, int32_t num_seqs, float* state_pool,
+                     const float* g, const float* beta, int32_t num_seqs, void* state_pool,
                      int64_t pool_row_stride, const int32_t* page_indices,
                      const int32_t* page_indptr, const int32_t* last_page_len,
                      int32_t page_size, const gdn_decode_slots_t* slots, void* o,
@@ -214,11 +221,11 @@ int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const
 int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const int32_t* cu_seqlens,
                 int32_t num_seqs, int64_t total_tokens,
-                const float* initial_state, int64_t initial_row_stride,
+                const void* initial_state, int64_t initial_row_stride,
                 const void* state_indices,
-                float* output_state, int64_t output_row_stride,
+                void* output_state, int64_t output_row_stride,
                 const void* output_state_indices, int32_t output_final_state,
-                float* state_checkpoints, int64_t checkpoint_row_stride,
+                void* state_checkpoints, int64_t checkpoint_row_stride,
                 const void* checkpoint_state_indices, const void* checkpoint_cu_starts,
                 const void* prefix_lens, int32_t checkpoint_every_n_tokens,
                 int32_t index_dtype, void* o, void* workspace, size_t workspace_bytes,
@@ -232,8 +239,8 @@ int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void
  */
 int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                const float* g, const float* beta, int32_t num_seqs,
-               const float* initial_state, int64_t initial_row_stride,
-               const void* initial_state_indices, float* output_state,
+               const void* initial_state, int64_t initial_row_stride,
+               const void* initial_state_indices, void* output_state,
                int64_t output_row_stride, const void* output_state_indices,
                int32_t index_dtype, void* o, hipStream_t stream);
 

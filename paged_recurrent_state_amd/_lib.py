@@ -30,7 +30,12 @@ class GDNError(RuntimeError):
 
 class Dims(C.Structure):
     _fields_ = [("num_qk_heads", C.c_int32), ("num_v_heads", C.c_int32),
-                ("head_dim_k", C.c_int32), ("head_dim_v", C.c_int32), ("scale", C.c_float)]
+                ("head_dim_k", C.c_int32), ("head_dim_v", C.c_int32), ("scale", C.c_float),
+                ("state_dtype", C.c_int32)]
+
+
+# element types of the state buffers (gdn_dims_t.state_dtype)
+STATE_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
 class _PrefillSlotsC(C.Structure):
@@ -141,8 +146,25 @@ def _index_dtype(*ts):
     raise TypeError("slot index tensors must be int32 or int64")
 
 
+def _state_dtype(dev, *named):
+    """The one element type (fp32 or bf16) of a call's state buffers."""
+    types = set()
+    for t, nm in named:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{nm} must be a tensor")
+        if t.dtype not in STATE_DTYPES:
+            raise TypeError(f"{nm} must be float32 or bfloat16, got {t.dtype}")
+        _need(t, nm, t.dtype, dev, contiguous=False)
+        types.add(t.dtype)
+    if len(types) > 1:
+        raise TypeError("all state buffers of a call must have one dtype")
+    return STATE_DTYPES[types.pop()] if types else 0
+
+
 def _pool_stride(pool: torch.Tensor, name: str, H: int, V: int, K: int) -> int:
-    """Row stride (floats) of a [rows, H, V, K] fp32 pool whose rows are dense."""
+    """Row stride (elements) of a [rows, H, V, K] pool whose rows are dense."""
     if pool.dim() != 4 or tuple(pool.shape[1:]) != (H, V, K):
         raise ValueError(f"{name} must be [rows, {H}, {V}, {K}], got {tuple(pool.shape)}")
     if pool.stride()[1:] != (V * K, K, 1):
@@ -150,10 +172,10 @@ def _pool_stride(pool: torch.Tensor, name: str, H: int, V: int, K: int) -> int:
     return pool.stride(0) if pool.shape[0] > 1 else H * V * K
 
 
-def _dims(q, v, scale):
+def _dims(q, v, scale, state_dtype: int = 0):
     Hqk, K = q.shape[-2], q.shape[-1]
     H, V = v.shape[-2], v.shape[-1]
-    return Dims(Hqk, H, K, V, float(scale) if scale else 0.0)
+    return Dims(Hqk, H, K, V, float(scale) if scale else 0.0, state_dtype)
 
 
 def _token_checks(q, k, v, g, beta, dev, T):
@@ -290,8 +312,7 @@ def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_i
     for t, nm in ((cu_seqlens, "cu_seqlens"), (page_indices, "page_indices"),
                   (page_indptr, "page_indptr"), (last_page_len, "last_page_len")):
         _need(t, nm, torch.int32, dev)
-    _need(state_pool, "state_pool", torch.float32, dev, contiguous=False)
-    d = _dims(q, v, scale)
+    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")))
     stride = _pool_stride(state_pool, "state_pool", d.num_v_heads, d.head_dim_v, d.head_dim_k)
     B = last_page_len.shape[0]
     o = out if out is not None else torch.empty(T, d.num_v_heads, d.head_dim_v,
@@ -321,8 +342,7 @@ def decode_paged(q, k, v, g, beta, state_pool, page_indices, page_indptr, page_s
     for t, nm in ((page_indices, "page_indices"), (page_indptr, "page_indptr"),
                   (last_page_len, "last_page_len")):
         _need(t, nm, torch.int32, dev)
-    _need(state_pool, "state_pool", torch.float32, dev, contiguous=False)
-    d = _dims(q, v, scale)
+    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")))
     stride = _pool_stride(state_pool, "state_pool", d.num_v_heads, d.head_dim_v, d.head_dim_k)
     o = out if out is not None else torch.empty(B, d.num_v_heads, d.head_dim_v,
                                                 dtype=torch.bfloat16, device=dev)
@@ -357,13 +377,13 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=N
                            "checkpoint_state_indices", "checkpoint_cu_starts", "prefix_lens")):
         if t is not None:
             _need(t, nm, t.dtype, dev)
-    d = _dims(q, v, scale)
+    bufs = ((initial_state, "initial_state"), (output_state, "output_state"),
+            (state_checkpoints, "state_checkpoints"))
+    d = _dims(q, v, scale, _state_dtype(dev, *bufs))
     H, V, K = d.num_v_heads, d.head_dim_v, d.head_dim_k
     strides = []
-    for t, nm in ((initial_state, "initial_state"), (output_state, "output_state"),
-                  (state_checkpoints, "state_checkpoints")):
+    for t, nm in bufs:
         if t is not None:
-            _need(t, nm, torch.float32, dev, contiguous=False)
             strides.append(_pool_stride(t, nm, H, V, K))
         else:
             strides.append(0)
@@ -394,14 +414,13 @@ def decode(q, k, v, g, beta, *, initial_state=None, initial_state_indices=None,
                   (output_state_indices, "output_state_indices")):
         if t is not None:
             _need(t, nm, t.dtype, dev)
-    d = _dims(q, v, scale)
+    d = _dims(q, v, scale, _state_dtype(dev, (initial_state, "initial_state"),
+                                        (output_state, "output_state")))
     H, V, K = d.num_v_heads, d.head_dim_v, d.head_dim_k
     s_in = s_out = 0
     if initial_state is not None:
-        _need(initial_state, "initial_state", torch.float32, dev, contiguous=False)
         s_in = _pool_stride(initial_state, "initial_state", H, V, K)
     if output_state is not None:
-        _need(output_state, "output_state", torch.float32, dev, contiguous=False)
         s_out = _pool_stride(output_state, "output_state", H, V, K)
     o = out if out is not None else torch.empty(B, H, V, dtype=torch.bfloat16, device=dev)
     _check(lib.gdn_decode(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B,

@@ -125,6 +125,9 @@ int check_dims(const gdn_dims_t* d) {
   if (d->num_v_heads % d->num_qk_heads != 0)
     return fail(GDN_EUNSUPPORTED, "v-heads (%d) must be a multiple of q/k heads (%d)",
                 d->num_v_heads, d->num_qk_heads);
+  if (d->state_dtype != GDN_STATE_F32 && d->state_dtype != GDN_STATE_BF16)
+    return fail(GDN_EINVAL, "state_dtype must be GDN_STATE_F32 or GDN_STATE_BF16 (got %d)",
+                d->state_dtype);
   return GDN_OK;
 }
 
@@ -155,8 +158,8 @@ SlotsDev carve_slots(void* ws, const WsLayout& L, int B) {
 // Launch the fused prefill once the rows are on the device.
 int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const int32_t* cu, int B,
-                const SlotsDev& sd, const WsLayout& L, void* ws, const float* init,
-                int64_t init_stride, float* out, int64_t out_stride, float* ckpt,
+                const SlotsDev& sd, const WsLayout& L, void* ws, const void* init,
+                int64_t init_stride, void* out, int64_t out_stride, void* ckpt,
                 int64_t ckpt_stride, const void* ckpt_idx, int ckpt_idx64, int ckpt_every,
                 void* o, hipStream_t stream) {
   PrefillParams pp;
@@ -179,6 +182,7 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.Hqk = d->num_qk_heads;
   pp.group = d->num_v_heads / d->num_qk_heads;
   pp.scale = eff_scale(d);
+  pp.state_bf16 = d->state_dtype == GDN_STATE_BF16;
   pp.init = init;
   pp.init_stride = init_stride;
   pp.out = out;
@@ -293,7 +297,7 @@ int gdn_csr_to_block_table(const int32_t* page_indptr, const int32_t* page_indic
 
 int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const int32_t* cu_seqlens,
-                      int32_t num_seqs, int64_t total_tokens, float* state_pool,
+                      int32_t num_seqs, int64_t total_tokens, void* state_pool,
                       int64_t pool_row_stride, const int32_t* page_indices,
                       const int32_t* page_indptr, const int32_t* last_page_len,
                       int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
@@ -341,7 +345,7 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
 }
 
 int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
-                     const float* g, const float* beta, int32_t num_seqs, float* state_pool,
+                     const float* g, const float* beta, int32_t num_seqs, void* state_pool,
                      int64_t pool_row_stride, const int32_t* page_indices,
                      const int32_t* page_indptr, const int32_t* last_page_len,
                      int32_t page_size, const gdn_decode_slots_t* slots, void* o,
@@ -366,6 +370,7 @@ int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const
   dp.Hqk = dims->num_qk_heads;
   dp.group = dims->num_v_heads / dims->num_qk_heads;
   dp.scale = eff_scale(dims);
+  dp.state_bf16 = dims->state_dtype == GDN_STATE_BF16;
   dp.init = state_pool;
   dp.init_stride = pool_row_stride;
   dp.out = state_pool;
@@ -391,10 +396,10 @@ int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const
 
 int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                 const float* g, const float* beta, const int32_t* cu_seqlens, int32_t num_seqs,
-                int64_t total_tokens, const float* initial_state, int64_t initial_row_stride,
-                const void* state_indices, float* output_state, int64_t output_row_stride,
+                int64_t total_tokens, const void* initial_state, int64_t initial_row_stride,
+                const void* state_indices, void* output_state, int64_t output_row_stride,
                 const void* output_state_indices, int32_t output_final_state,
-                float* state_checkpoints, int64_t checkpoint_row_stride,
+                void* state_checkpoints, int64_t checkpoint_row_stride,
                 const void* checkpoint_state_indices, const void* checkpoint_cu_starts,
                 const void* prefix_lens, int32_t checkpoint_every_n_tokens, int32_t index_dtype,
                 void* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -446,9 +451,9 @@ int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void
 }
 
 int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
-               const float* g, const float* beta, int32_t num_seqs, const float* initial_state,
+               const float* g, const float* beta, int32_t num_seqs, const void* initial_state,
                int64_t initial_row_stride, const void* initial_state_indices,
-               float* output_state, int64_t output_row_stride, const void* output_state_indices,
+               void* output_state, int64_t output_row_stride, const void* output_state_indices,
                int32_t index_dtype, void* o, hipStream_t stream) {
   if (int rc = check_dims(dims)) return rc;
   if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0");
@@ -479,6 +484,7 @@ int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void*
   dp.rd_idx = initial_state_indices;
   dp.wr_idx = output_state_indices;
   dp.idx64 = index_dtype == GDN_INDEX_INT64;
+  dp.state_bf16 = dims->state_dtype == GDN_STATE_BF16;
   dp.init = initial_state;
   dp.init_stride = initial_row_stride;
   dp.out = output_state;

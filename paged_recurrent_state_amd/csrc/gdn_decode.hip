@@ -13,11 +13,13 @@
 // starts from literal zeros; a write row of -1 skips the store.
 //
 // Layout: one 256-thread workgroup per (sequence, head).  Each 16-lane group
-// owns one 512-byte state row at a time: lane c holds k = 4c..4c+3 and
-// 64+4c..64+4c+3, so one 16-byte load instruction covers 4 whole rows and
-// the row's dot products reduce inside the 16-lane group with 4 DPP steps
-// (no LDS traffic).  16 rows per workgroup per step, all 8 steps' loads
-// issued before any arithmetic.
+// owns one state row at a time: for an fp32 state (512-byte rows) lane c
+// holds k = 4c..4c+3 and 64+4c..64+4c+3, so one 16-byte load instruction
+// covers 4 whole rows; for a bf16 state (256-byte rows) lane c holds
+// k = 8c..8c+7, one 16-byte load a row.  The row's dot products reduce inside
+// the 16-lane group with 4 DPP steps (no LDS traffic).  16 rows per workgroup
+// per step, all 8 steps' loads issued before any arithmetic; the update runs
+// in fp32 either way and a bf16 row is stored rounded to nearest even.
 // Loads and stores bypass the caches' retention (non-temporal): every byte is
 // touched once.
 #include "gdn_internal.h"
@@ -53,7 +55,15 @@ __device__ __forceinline__ void unpack4(u32x2 w, float (&f)[4]) {
   f[2] = bf2f(u16(w.y & 0xffffu));
   f[3] = bf2f(u16(w.y >> 16));
 }
+__device__ __forceinline__ void unpack8(u32x4 w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
 
+template <bool BF16>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
   const int bid = blockIdx.x;
   const int b = bid / p.H;
@@ -62,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int g = lane >> 4;  // row within the wave's 4 rows of a step
-  const int c = lane & 15;  // k = 4c..4c+3 and 64+4c..64+4c+3
+  const int c = lane & 15;  // k = 4c..4c+3 and 64+4c..64+4c+3 (fp32), 8c..8c+7 (bf16)
 
   int64_t rd, wr;
   if (p.mode == 1) {
@@ -78,7 +88,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
 
   const int hq = h / p.group;
   float k8[8], q8[8];
-  {
+  if constexpr (BF16) {
+    const u16* kp = p.k + ((int64_t)b * p.Hqk + hq) * kDim + 8 * c;
+    const u16* qp = p.q + ((int64_t)b * p.Hqk + hq) * kDim + 8 * c;
+    unpack8(*(const u32x4*)kp, k8);
+    unpack8(*(const u32x4*)qp, q8);
+  } else {
     const u16* kp = p.k + ((int64_t)b * p.Hqk + hq) * kDim + 4 * c;
     const u16* qp = p.q + ((int64_t)b * p.Hqk + hq) * kDim + 4 * c;
     float t[4];
@@ -96,18 +111,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   const float bt = p.beta ? p.beta[bh] : 1.f;
 
   // step it covers rows 16*it + 4*wid + g
-  f32x4 s[kSteps][2];
+  f32x4 s[kSteps][2];  // fp32 rows
+  u32x4 sb[kSteps];    // bf16 rows
   if (rd >= 0) {
-    const float* src = p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * c;
+    if constexpr (BF16) {
+      const u16* src = (const u16*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 8 * c;
 #pragma unroll
-    for (int it = 0; it < kSteps; ++it) {
-      const int row = 16 * it + 4 * wid + g;
-      s[it][0] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
-      s[it][1] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim + 64));
+      for (int it = 0; it < kSteps; ++it)
+        sb[it] = __builtin_nontemporal_load((const u32x4*)(src + (16 * it + 4 * wid + g) * kDim));
+    } else {
+      const float* src = (const float*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * c;
+#pragma unroll
+      for (int it = 0; it < kSteps; ++it) {
+        const int row = 16 * it + 4 * wid + g;
+        s[it][0] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
+        s[it][1] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim + 64));
+      }
     }
   } else {
 #pragma unroll
-    for (int it = 0; it < kSteps; ++it) s[it][0] = s[it][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < kSteps; ++it) {
+      s[it][0] = s[it][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[it] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   float vv[kSteps];
 #pragma unroll
@@ -118,28 +144,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   for (int i = 0; i < 8; ++i) kq += k8[i] * q8[i];
   kq = sum16(kq);
 
-  float* dst = wr >= 0 ? p.out + wr * p.out_stride + (int64_t)h * kDim * kDim + 4 * c : nullptr;
+  const int64_t doff = wr >= 0 ? wr * p.out_stride + (int64_t)h * kDim * kDim : 0;
   float o_mine = 0.f;  // o of row 16*c + 4*wid + g (lanes c < 8)
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     const int row = 16 * it + 4 * wid + g;
+    float sv[8];  // the lane's 8 state values, in k8's order
+    if constexpr (BF16) {
+      unpack8(sb[it], sv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = s[it][i >> 2][i & 3];
+    }
     float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sk += s[it][hh][i] * k8[4 * hh + i];
-        sq += s[it][hh][i] * q8[4 * hh + i];
-      }
+    for (int i = 0; i < 8; ++i) {
+      sk += sv[i] * k8[i];
+      sq += sv[i] * q8[i];
+    }
     sk = sum16(sk);
     sq = sum16(sq);
     const float delta = bt * (vv[it] - alpha * sk);
+    float y[8];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      f32x4 y;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = alpha * s[it][hh][i] + delta * k8[4 * hh + i];
-      if (dst) __builtin_nontemporal_store(y, (f32x4*)(dst + row * kDim + 64 * hh));
+    for (int i = 0; i < 8; ++i) y[i] = alpha * sv[i] + delta * k8[i];
+    if (wr >= 0) {
+      if constexpr (BF16) {
+        u16* dst = (u16*)p.out + doff + 8 * c;
+        __builtin_nontemporal_store(u32x4{f2bf2(y[0], y[1]), f2bf2(y[2], y[3]), f2bf2(y[4], y[5]), f2bf2(y[6], y[7])},
+                                    (u32x4*)(dst + row * kDim));
+      } else {
+        float* dst = (float*)p.out + doff + 4 * c;
+        __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]}, (f32x4*)(dst + row * kDim));
+        __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]}, (f32x4*)(dst + row * kDim + 64));
+      }
     }
     if (c == it) o_mine = p.scale * (alpha * sq + delta * kq);
   }
@@ -151,7 +189,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0) return hipSuccess;
-  decode_kernel<<<(unsigned)blocks, kThreads, 0, s>>>(p);
+  if (p.state_bf16) decode_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(p);
+  else decode_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

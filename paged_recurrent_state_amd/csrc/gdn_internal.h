@@ -65,11 +65,13 @@ struct PrefillParams {
   int Hqk;
   int group;  // H / Hqk
   float scale;
-  const float* init;
+  // state buffers: fp32, or bf16 when state_bf16 (strides in elements)
+  int state_bf16;
+  const void* init;
   int64_t init_stride;
-  float* out;
+  void* out;
   int64_t out_stride;
-  float* ckpt;
+  void* ckpt;
   int64_t ckpt_stride;
   const void* ckpt_idx;
   int ckpt_idx64;
@@ -108,9 +110,11 @@ struct DecodeParams {
   const int32_t* page_indices;
   const int32_t* page_indptr;
   const int32_t* last_page_len;
-  const float* init;
+  // state buffers: fp32, or bf16 when state_bf16 (strides in elements)
+  int state_bf16;
+  const void* init;
   int64_t init_stride;
-  float* out;
+  void* out;
   int64_t out_stride;
 };
 

@@ -470,6 +470,36 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&accS)[8], 
   for (int mb = 0; mb < 8; ++mb) *(f32x4*)(dst + state_k(mb, gq)) = accS[mb];
 }
 
+// The lane's state row in a caller's state buffer (fp32, or bf16 rounded to
+// nearest even when bf16), element offset `off` = the row's k = 0
+__device__ __forceinline__ void store_state_buf(void* base, int64_t off, const f32x4 (&accS)[8], int gq,
+                                                bool bf16) {
+  if (bf16) {
+    u16* dst = (u16*)base + off;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      *(u32x2*)(dst + state_k(mb, gq)) = u32x2{f2bf2(accS[mb][0], accS[mb][1]), f2bf2(accS[mb][2], accS[mb][3])};
+  } else {
+    store_state((float*)base + off, accS, gq);
+  }
+}
+__device__ __forceinline__ void load_state_buf(const void* base, int64_t off, f32x4 (&accS)[8], int gq,
+                                               bool bf16) {
+  if (bf16) {
+    const u16* src = (const u16*)base + off;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const u32x2 w = *(const u32x2*)(src + state_k(mb, gq));
+      accS[mb] = f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    }
+  } else {
+    const float* src = (const float*)base + off;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) accS[mb] = *(const f32x4*)(src + state_k(mb, gq));
+  }
+}
+
 struct RecSmem {
   u16 Kb[2][kTileWords];               // K tiles, double-buffered by chunk parity
   u16 Qb[2][kTileWords];               // Q tiles
@@ -625,9 +655,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) accS[mb][r] = state_k(mb, gq) + r == vrow ? 1.f : 0.f;
   } else if (rd >= 0 && p.init) {
-    const float* src = p.init + (int64_t)rd * p.init_stride + head_off;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) accS[mb] = *(const f32x4*)(src + state_k(mb, gq));
+    load_state_buf(p.init, (int64_t)rd * p.init_stride + head_off, accS, gq, p.state_bf16);
   } else if (rd <= -2) {  // a state of the sequence-parallel workspace
     const float* src = p.ws_state + (int64_t)(-2 - rd) * p.ws_state_stride + head_off;
 #pragma unroll
@@ -695,7 +723,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       load_tile<16 / NW>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
       if (outs) load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
-    if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
+    if (ckpt_row >= 0) store_state_buf(p.ckpt, ckpt_row * p.ckpt_stride + head_off, accS, gq, p.state_bf16);
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
     // Each MFMA run below has vector work beside it that does not depend on
@@ -951,7 +979,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
           acc[f >> 1] = mfma16x16x32(kt, rh[f & 1], acc[f >> 1]);
           acc[f >> 1] = mfma16x16x32(kt, rl[f & 1], acc[f >> 1]);
         }
-        store_state(p.ckpt + row * p.ckpt_stride + head_off, acc, gq);
+        store_state_buf(p.ckpt, row * p.ckpt_stride + head_off, acc, gq, p.state_bf16);
       }
       const float gC = sc[2][kChunk - 1];
 #pragma unroll
@@ -996,8 +1024,8 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     if constexpr (NW == 8) write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
     else write_o_tile<NW>(p, sm, s, nbase + kChunk * (nch - 1), 16 * NW * vt, tid);
   }
-  if (ckpt_row >= 0) store_state(p.ckpt + ckpt_row * p.ckpt_stride + head_off, accS, gq);
-  if (wr >= 0 && p.out) store_state(p.out + (int64_t)wr * p.out_stride + head_off, accS, gq);
+  if (ckpt_row >= 0) store_state_buf(p.ckpt, ckpt_row * p.ckpt_stride + head_off, accS, gq, p.state_bf16);
+  if (wr >= 0 && p.out) store_state_buf(p.out, (int64_t)wr * p.out_stride + head_off, accS, gq, p.state_bf16);
   if (wr <= -2) store_state(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, accS, gq);
 }
 
@@ -1132,9 +1160,19 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   // start_0: the sequence's initial state (a row of the caller's buffer or zero)
   f32x4 i0 = {0.f, 0.f, 0.f, 0.f}, i1 = i0;
   if (rd >= 0 && p.init) {
-    const float* s0 = p.init + (int64_t)rd * p.init_stride + hoff + (int64_t)(16 * rb + r) * kDim;
-    i0 = *(const f32x4*)(s0 + c0);
-    i1 = *(const f32x4*)(s0 + 64 + c0);
+    const int64_t off = (int64_t)rd * p.init_stride + hoff + (int64_t)(16 * rb + r) * kDim;
+    if (p.state_bf16) {
+      const u16* s0 = (const u16*)p.init + off;
+      const u32x2 w0 = *(const u32x2*)(s0 + c0), w1 = *(const u32x2*)(s0 + 64 + c0);
+      i0 = f32x4{__uint_as_float(w0.x << 16), __uint_as_float(w0.x & 0xffff0000u),
+                 __uint_as_float(w0.y << 16), __uint_as_float(w0.y & 0xffff0000u)};
+      i1 = f32x4{__uint_as_float(w1.x << 16), __uint_as_float(w1.x & 0xffff0000u),
+                 __uint_as_float(w1.y << 16), __uint_as_float(w1.y & 0xffff0000u)};
+    } else {
+      const float* s0 = (const float*)p.init + off;
+      i0 = *(const f32x4*)(s0 + c0);
+      i1 = *(const f32x4*)(s0 + 64 + c0);
+    }
   }
   *(f32x4*)&sm.S[r][c0] = i0;
   *(f32x4*)&sm.S[r][64 + c0] = i1;

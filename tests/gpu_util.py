@@ -33,7 +33,7 @@ def check_outputs(o_gpu: torch.Tensor, o_ref: np.ndarray, what: str = "o"):
 
 
 def check_state(s_gpu, s_ref: np.ndarray, what: str = "state"):
-    s = s_gpu.detach().cpu().numpy().astype(np.float64) if isinstance(s_gpu, torch.Tensor) \
+    s = s_gpu.detach().float().cpu().numpy().astype(np.float64) if isinstance(s_gpu, torch.Tensor) \
         else np.asarray(s_gpu, dtype=np.float64)
     assert np.isfinite(s).all(), f"{what}: non-finite values"
     rf = rel_fro(s, s_ref)
@@ -42,21 +42,23 @@ def check_state(s_gpu, s_ref: np.ndarray, what: str = "state"):
 
 
 def changed_rows(before: torch.Tensor, after: torch.Tensor, block: int = 512):
-    """Rows of a [rows, H, V, K] fp32 pool whose bits differ (on device, in blocks)."""
+    """Rows of a [rows, H, V, K] fp32 or bf16 pool whose bits differ (on device, in blocks)."""
     out = []
+    bits = torch.int32 if before.element_size() == 4 else torch.int16
     for r0 in range(0, before.shape[0], block):
-        a = before[r0:r0 + block].view(torch.int32).reshape(-1, before[0].numel())
-        b = after[r0:r0 + block].view(torch.int32).reshape(-1, after[0].numel())
+        a = before[r0:r0 + block].view(bits).reshape(-1, before[0].numel())
+        b = after[r0:r0 + block].view(bits).reshape(-1, after[0].numel())
         out.extend((r0 + torch.nonzero((a != b).any(dim=1)).flatten()).tolist())
     return sorted(out)
 
 
 def pool_rows_cpu(pool: torch.Tensor, rows):
-    """fp32 CPU copy of selected rows (oracle input), as a dict-like array."""
+    """fp32 CPU copy of selected rows (oracle input; bf16 rows convert exactly),
+    as a dict-like array."""
     rows = sorted(set(int(r) for r in rows if int(r) >= 0))
     out = {}
     for r in rows:
-        out[r] = pool[r].detach().cpu().numpy()
+        out[r] = pool[r].detach().float().cpu().numpy()
     return out
 
 

@@ -180,3 +180,10 @@ def test_table_conversions_reject_bad_args(lib):
     assert lib.gdn_csr_to_block_table(f, f, f, 2, -16, 4, f, 8, f, None, None) == -1
     assert lib.gdn_csr_to_block_table(f, f, f, 2, 16, 9, f, 8, f, None, None) == -1
     assert lib.gdn_csr_to_block_table(f, f, None, 2, 16, 4, f, 8, f, None, None) == -1
+
+
+def test_bad_state_dtype(lib):
+    d = dims()
+    d.state_dtype = 2
+    assert _prefill_paged(lib, d) == -1
+    assert b"state_dtype" in lib.gdn_last_error()

@@ -32,11 +32,16 @@ def run_prefill_paged(pre, pool, slots=None, scale=None):
                            pre["page_size"], pre["last_page_len"], slots=slots, scale=scale)
 
 
-def oracle_prefill_paged(pre, pool_rows):
+def state_dtype_of(pool):
+    return "bf16" if pool.dtype == torch.bfloat16 else "fp32"
+
+
+def oracle_prefill_paged(pre, pool_rows, state_dtype="fp32"):
     return ogdn.prefill_paged(pre["q"].cpu(), pre["k"].cpu(), pre["v"].cpu(), pre["g"].cpu(),
                               pre["beta"].cpu(), pre["cu_seqlens"].cpu(), RowView(pool_rows),
                               pre["page_indices"].cpu(), pre["page_indptr"].cpu(),
-                              pre["last_page_len"].cpu(), pre["page_size"])
+                              pre["last_page_len"].cpu(), pre["page_size"],
+                              state_dtype=state_dtype)
 
 
 def check_paged_prefill(pre, pool):
@@ -46,7 +51,7 @@ def check_paged_prefill(pre, pool):
     before = pool.clone()
     o = run_prefill_paged(pre, pool)
     torch.cuda.synchronize()
-    o_ref, writes, _ = oracle_prefill_paged(pre, rows_in)
+    o_ref, writes, _ = oracle_prefill_paged(pre, rows_in, state_dtype_of(pool))
     check_outputs(o, o_ref)
     assert changed_rows(before, pool) == sorted(writes), "page-write set differs"
     errs = [check_state(pool[r], s, f"row {r}") for r, s in writes.items()]
@@ -422,3 +427,120 @@ def test_prefill_sequence_parallel(m, waves):
     finally:
         os.environ.pop("GDN_PREFILL_SPLIT_CHUNKS", None)
         os.environ.pop("GDN_PREFILL_TILE_WAVES", None)
+
+
+# ---- bf16 state pools: states stored rounded to bf16, arithmetic in fp32
+
+@pytest.mark.parametrize("split", [None, "2"])
+def test_bf16_pool_prefill(split):
+    """Paged prefill on a bf16 pool (whole sequences, and forced segments of
+    2 chunks): bf16 read rows, rounded page-boundary and final stores, the
+    write set and every untouched row bit for bit."""
+    if split:
+        os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = split
+    try:
+        pre, pool = make_case([0, 37, 128, 1000], [700, 1, 64, 900], ps=128, H=4, Hqk=2,
+                              seed=31, g_scale=0.3)
+        pool = pool.to(torch.bfloat16)
+        _, writes, err = check_paged_prefill(pre, pool)
+        assert len(writes) > 4
+        print(f"bf16 pool prefill (split {split}): worst state rel {err:.2e}")
+    finally:
+        os.environ.pop("GDN_PREFILL_SPLIT_CHUNKS", None)
+
+
+def test_bf16_pool_prefill_then_decode():
+    c = cuda(workloads.config0())
+    pool = c["pool"].to(torch.bfloat16)
+    pre = c["prefill"]
+    _, writes, _ = check_paged_prefill(pre, pool)
+    assert sorted(writes) == [4, 5, 9, 11, 14]
+    m = lib()
+    dec = c["decode"]
+    rows_in = pool_rows_cpu(pool, dec["read_rows"])
+    before = pool.clone()
+    od = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
+                        dec["page_indices"], dec["page_indptr"], 128, dec["last_page_len"])
+    torch.cuda.synchronize()
+    od_ref, dwrites, _ = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
+                                           dec["g"].cpu(), dec["beta"].cpu(), RowView(rows_in),
+                                           dec["page_indices"].cpu(), dec["page_indptr"].cpu(),
+                                           dec["last_page_len"].cpu(), state_dtype="bf16")
+    check_outputs(od, od_ref)
+    assert changed_rows(before, pool) == sorted(dwrites)
+    for r, st in dwrites.items():
+        check_state(pool[r], st)
+
+
+def test_bf16_pool_decode_batch():
+    """64 sequences (16 opening a new page) on a bf16 pool, GQA 16 -> 32 heads."""
+    m = lib()
+    c = workloads.config2(device=DEV, num_seqs=64, num_pages=2048, new_page_seqs=16)
+    pool = c["pool"].to(torch.bfloat16)
+    del c["pool"]
+    d = c["decode"]
+    rows_in = pool_rows_cpu(pool, d["read_rows"])
+    before = pool.clone()
+    o = m.decode_paged(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, d["page_indices"],
+                       d["page_indptr"], 1024, d["last_page_len"])
+    torch.cuda.synchronize()
+    o_ref, writes, _ = ogdn.decode_paged(d["q"].cpu(), d["k"].cpu(), d["v"].cpu(), d["g"].cpu(),
+                                         d["beta"].cpu(), RowView(rows_in), d["page_indices"].cpu(),
+                                         d["page_indptr"].cpu(), d["last_page_len"].cpu(),
+                                         state_dtype="bf16")
+    check_outputs(o, o_ref)
+    assert changed_rows(before, pool) == sorted(writes)
+    worst = max(check_state(pool[r], st) for r, st in writes.items())
+    print(f"bf16 pool decode batch: worst state rel {worst:.2e}")
+
+
+def test_bf16_general_prefill_checkpoints():
+    """Slot-argument prefill in pieces on bf16 state buffers with checkpoints
+    every 100 tokens (inside chunks) into a separate bf16 buffer."""
+    m = lib()
+    H = 2
+    N = 100
+    c = cuda(workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N,
+                               num_rows=3, g_scale=0.1))
+    slot_pool = c["pool"].to(torch.bfloat16)
+    ckpt = workloads.nan_pool(1000 // N, H, 128, 128, device=DEV).to(torch.bfloat16)
+    ref_slot = np.zeros((3, H, 128, 128))
+    ref_ck = {}
+    for call in c["calls"]:
+        o = m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"], call["cu_seqlens"],
+                      initial_state=slot_pool, state_indices=call["state_indices"],
+                      output_state=slot_pool, output_state_indices=call["output_state_indices"],
+                      output_final_state=True, state_checkpoints=ckpt,
+                      checkpoint_state_indices=c["checkpoint_state_indices"],
+                      checkpoint_cu_starts=call["checkpoint_cu_starts"],
+                      prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=N)
+        torch.cuda.synchronize()
+        res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(), call["g"].cpu(),
+                           call["beta"].cpu(), call["cu_seqlens"].cpu(), initial_state=ref_slot,
+                           state_indices=call["state_indices"].tolist(), output_final_state=True,
+                           output_state_indices=call["output_state_indices"].tolist(),
+                           checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
+                           checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
+                           prefix_lens=call["prefix_lens"].tolist(), checkpoint_every_n_tokens=N,
+                           shared_pool=False, state_dtype="bf16")
+        check_outputs(o, res.o)
+        ref_slot = ogdn.apply_writes(ref_slot, res.final)
+        ref_ck.update(res.checkpoints)
+        check_state(slot_pool[c["slot"]], ref_slot[c["slot"]], "slot")
+    got = [r for r in range(1000 // N) if torch.isfinite(ckpt[r].float()).all()]
+    assert got == sorted(ref_ck)
+    for r, st in ref_ck.items():
+        check_state(ckpt[r], st, f"checkpoint {r}")
+
+
+def test_state_buffers_share_one_dtype():
+    m = lib()
+    gen = workloads.generator(5)
+    t = cuda(workloads.token_inputs(64, 2, 2, 128, 128, gen))
+    cu = torch.tensor([0, 64], dtype=torch.int32, device=DEV)
+    a = torch.zeros(1, 2, 128, 128, device=DEV)
+    with pytest.raises(TypeError):
+        m.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, initial_state=a,
+                  output_state=a.to(torch.bfloat16), output_final_state=True)
+    with pytest.raises(TypeError):
+        m.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, initial_state=a.half())
