@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--workload", default="hybrid", choices=["hybrid", "prefill", "decode", "long"])
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side measurements (bf16-pool decode, long single prompt)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--cpu-sample-decode", type=int, default=128)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -155,6 +157,70 @@ def cpu_baseline(pre_cpu, dec_cpu, pool_rows, sample_tokens, sample_decode, laye
 
 
 # ----------------------------------------------------------------- workloads
+def _median_ms(torch, run, n, reps=3):
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    res = []
+    for _ in range(reps):
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / n)
+    return sorted(res)[len(res) // 2]
+
+
+def side_measurements(torch, gdn, workloads, pool, dec, ps, H, Hqk, t_dc_ms):
+    """Timed beside the step, not part of it: the decode batch on a bf16 copy
+    of the pool (the same rows at half the bytes), and the long single prompt
+    (one sequence, 32 heads, 32768 tokens in 5 calls) with the
+    sequence-parallel recurrence against whole sequences."""
+    dev = pool.device
+    out = {}
+    Bd = int(dec["last_page_len"].shape[0])
+    o = torch.empty(Bd, H, D, dtype=torch.bfloat16, device=dev)
+    sl = gdn.decode_slots(dec["page_indices"], dec["page_indptr"], dec["last_page_len"])
+    pool16 = pool.to(torch.bfloat16)
+    ms = _median_ms(torch, lambda: gdn.decode_paged(
+        dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool16, dec["page_indices"],
+        dec["page_indptr"], ps, dec["last_page_len"], slots=sl, out=o), 20)
+    del pool16
+    by = decode_bytes(Bd, H, Hqk) - Bd * H * STATE_BYTES  # state rows at 2 bytes an element
+    out["bf16_pool_decode"] = {
+        "workload": f"the step's decode batch ({Bd} seqs, H={H}) on a bf16 copy of the pool",
+        "ms": ms, "state_GBps": by / (ms / 1e3) / 1e9,
+        "frac_hbm_peak": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "fp32_pool_ms": t_dc_ms}
+    c = workloads.config3(device=dev)
+
+    def run():
+        for call in c["calls"]:
+            gdn.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
+                        call["cu_seqlens"], initial_state=c["pool"],
+                        state_indices=call["state_indices"], output_state=c["pool"],
+                        output_state_indices=call["output_state_indices"],
+                        output_final_state=True, state_checkpoints=c["state_checkpoints"],
+                        checkpoint_state_indices=c["checkpoint_state_indices"],
+                        checkpoint_cu_starts=call["checkpoint_cu_starts"],
+                        prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=c["every_n"])
+    T = sum(int(call["q"].shape[0]) for call in c["calls"])
+    ms_split = _median_ms(torch, run, 5)
+    os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = "0"
+    try:
+        ms_whole = _median_ms(torch, run, 5)
+    finally:
+        del os.environ["GDN_PREFILL_SPLIT_CHUNKS"]
+    out["long_prompt"] = {
+        "workload": f"one sequence, H=Hqk={c['H']}, {T} tokens in {len(c['calls'])} calls, "
+                    f"checkpoints every {c['every_n']}",
+        "sequence_parallel_ms": ms_split, "prefill_tokens_per_s": T / (ms_split / 1e3),
+        "whole_sequence_ms": ms_whole, "speedup": ms_whole / ms_split}
+    return out
+
+
 def hybrid(args, torch, gdn, workloads):
     dev = "cuda"
     L = args.layers
@@ -254,6 +320,8 @@ def hybrid(args, torch, gdn, workloads):
         "prefill_ms_per_layer": t_pf_ms, "decode_ms_per_layer": t_dc_ms,
         "roofline": roof,
     }
+    if not args.no_side:
+        line["side"] = side_measurements(torch, gdn, workloads, pool, dec0, ps, H, Hqk, t_dc_ms)
     cpu_inputs = None
     if not args.no_cpu_baseline:
         pcpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pre0.items()}
