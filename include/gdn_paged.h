@@ -40,7 +40,9 @@
  *
  * Supported: K = V = 128, H a multiple of Hqk, page_size a positive multiple
  * of 64, any positive checkpoint_every_n_tokens (a checkpoint inside a 64-token
- * chunk costs one more state-update product in that chunk).
+ * chunk costs one more state-update product in that chunk).  Token positions
+ * are 32-bit: a sequence's prefix plus its new tokens, and the checkpoint
+ * positions up to it plus checkpoint_every_n_tokens, stay below 2^31.
  */
 #ifndef GDN_PAGED_H
 #define GDN_PAGED_H
