@@ -27,10 +27,10 @@ struct SlotsDev {
 constexpr int kFragElems = 64 * 8;  // one 16x16x32 MFMA operand fragment, bf16 elements
 
 // Per (chunk slot, v-head) record the intra-chunk kernel hands to the
-// recurrence: T diag(beta), T = (I + A)^-1, as its 6 nonzero hi and 6 lo bf16
-// operand fragments, and the per-row scalars beta, G (log2 units), gamma =
-// 2^G, exp(G_last - G).
-constexpr int kRecWords = 2 * 6 * kFragElems;  // bf16 elements (12 KiB): T's 6 nonzero fragments, hi and lo
+// recurrence: T diag(beta), T = (I + A)^-1, as 5 hi and 5 lo bf16 operand
+// fragments (its 6 nonzero ones, two half-empty ones sharing one), and the
+// per-row scalars beta, G (log2 units), gamma = 2^G, exp(G_last - G).
+constexpr int kRecWords = 2 * 5 * kFragElems;  // bf16 elements (10 KiB)
 constexpr int kRecScal = 4 * kChunk;           // floats (1 KiB)
 
 // Sequence-parallel recurrence (long sequences in batches too small to fill

@@ -49,11 +49,26 @@ constexpr int kKtWordsL = 8 * 2 * kFragElems;   // K^T fragments
 constexpr int kMatFrag = 8 * kFragElems;        // one 64x64 operand (8 fragments)
 
 // T is lower triangular: of its 8 operand fragments (row block mt, k-step
-// ks) the two with mt < 2, ks = 1 are zero.  The record keeps the other 6,
-// hi halves then lo halves.
-constexpr int kTFrags = 6;
+// ks) the two with mt < 2, ks = 1 are zero, and two more, (0, 0) and (2, 1),
+// are zero in slots 4..7 of every lane (the blocks above the diagonal).  The
+// record keeps 5: (0, 0) and (2, 1) share fragment 0 (slots 0..3 of each),
+// then (1, 0), (2, 0), (3, 0), (3, 1); hi halves then lo halves.
+constexpr int kTFrags = 5;
 static_assert(kRecWords == 2 * kTFrags * kFragElems, "T record size");
+// operand slot of nonzero fragment (mt, ks) in the unpacked set of 6
 __device__ __forceinline__ int t_slot(int mt, int ks) { return mt < 2 ? mt : 2 * mt - 2 + ks; }
+
+// The 6 nonzero operand fragments of T from the record's 5: slots 0 and 3
+// take their nonzero halves out of fragment 0.
+__device__ __forceinline__ void unpack_t(const bf16x8 (&r)[kTFrags], bf16x8 (&t)[6]) {
+  const u32x4 w = __builtin_bit_cast(u32x4, r[0]);
+  t[0] = as_bf16x8(u32x4{w[0], w[1], 0u, 0u});
+  t[1] = r[1];
+  t[2] = r[2];
+  t[3] = as_bf16x8(u32x4{w[2], w[3], 0u, 0u});
+  t[4] = r[3];
+  t[5] = r[4];
+}
 
 // Fragment-ordered 64x128 tile: element (t, k) sits in fragment (t/16, k/32),
 // lane (t%16) + 16*gq, slot j, where k%32 = 16*(j/4) + 4*gq + j%4 (perm_row).
@@ -422,36 +437,27 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   }
   __syncthreads();
 
-  // T's 6 nonzero fragments (hi/lo) straight to the workspace
+  // the record's 5 fragments of T diag(beta) (hi/lo) straight to the
+  // workspace: slots 4h..4h+3 of record fragment f hold columns 4g4..4g4+3
+  // of block (bi, bj) = (0, 0), (2, 2) for f = 0 and (mt, 2 (f == 4) + h)
+  // with mt = 1, 2, 3, 3 for f = 1..4 (lane = row within the block + 16 g4)
   u16* Tw = p.ws_T + ch * kRecWords;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int frag = wid + 4 * i;  // wave-uniform
-    const int mt = frag >> 1, ks = frag & 1;
-    if (mt < 2 && ks == 1) continue;  // all zero
+  for (int f = wid; f < kTFrags; f += 4) {
     const int rr = lane & 15, g4 = lane >> 4;
-    // slots 4h..4h+3: columns 32ks + 16h + 4g4 .. +3 of block (mt, 2ks + h);
-    // blocks above the diagonal are zero, and so is the upper triangle of
-    // the diagonal blocks (exactly, from the substitution)
     float vals[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int bj = 2 * ks + h, c0 = 16 * bj + 4 * g4;
-      if (bj <= mt) {
-        const f32x4 tv = *(const f32x4*)&sm.u.AT[tri_idx(mt, bj)][rr][4 * g4];
-        const f32x4 bv = *(const f32x4*)&sm.B[c0];
+      const int bi = f == 0 ? 2 * h : (f < 3 ? f : 3);
+      const int bj = f == 0 ? 2 * h : (f == 4 ? 2 : 0) + h;
+      const f32x4 tv = *(const f32x4*)&sm.u.AT[tri_idx(bi, bj)][rr][4 * g4];
+      const f32x4 bv = *(const f32x4*)&sm.B[16 * bj + 4 * g4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vals[4 * h + e] = tv[e] * bv[e];  // T diag(beta)
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vals[4 * h + e] = 0.f;
-      }
+      for (int e = 0; e < 4; ++e) vals[4 * h + e] = tv[e] * bv[e];  // T diag(beta)
     }
     bf16x8 hi, lo;
     split8(vals, hi, lo);
-    const int slot = t_slot(mt, ks);
-    *(bf16x8*)(Tw + (slot * 64 + lane) * 8) = hi;
-    *(bf16x8*)(Tw + kTFrags * kFragElems + (slot * 64 + lane) * 8) = lo;
+    *(bf16x8*)(Tw + (f * 64 + lane) * 8) = hi;
+    *(bf16x8*)(Tw + kTFrags * kFragElems + (f * 64 + lane) * 8) = lo;
   }
 }
 
@@ -836,11 +842,16 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     // on P's exponent)
     f32x4 E[4];
     {
-      bf16x8 th[kTFrags], tl[kTFrags];
+      bf16x8 th[6], tl[6];
+      {
+        bf16x8 rh[kTFrags], rl[kTFrags];
 #pragma unroll
-      for (int f = 0; f < kTFrags; ++f) {
-        th[f] = lds_frag(Tf, f, lane);
-        tl[f] = lds_frag(Tf + kTFrags * kFragElems, f, lane);
+        for (int f = 0; f < kTFrags; ++f) {
+          rh[f] = lds_frag(Tf, f, lane);
+          rl[f] = lds_frag(Tf + kTFrags * kFragElems, f, lane);
+        }
+        unpack_t(rh, th);
+        unpack_t(rl, tl);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) E[mt] = f32x4{0.f, 0.f, 0.f, 0.f};

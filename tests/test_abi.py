@@ -61,7 +61,7 @@ def test_workspace_size(lib, monkeypatch):
     # T record (6 fragments, hi and lo) + scalars per (slot, head), and a
     # 16-byte chunk-table entry per slot (regions rounded up to 256 bytes)
     al = lambda x: (x + 255) // 256 * 256
-    assert b - a == 100 * 4 * (12288 + 1024) + al(103 * 16) - al(3 * 16)
+    assert b - a == 100 * 4 * (10240 + 1024) + al(103 * 16) - al(3 * 16)
     bad = dims(K=64)
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
 
