@@ -239,10 +239,14 @@ def hybrid(args, torch, gdn, workloads):
     stream = torch.cuda.current_stream()
     E = torch.cuda.Event
 
-    def step(events=None):
+    def step(events=None, slot_events=None):
+        if slot_events is not None:
+            slot_events[0].record(stream)
         sl_p = gdn.prefill_slots(pre0["cu_seqlens"], pre0["page_indices"], pre0["page_indptr"],
                                  pre0["last_page_len"], ps)
         sl_d = gdn.decode_slots(dec0["page_indices"], dec0["page_indptr"], dec0["last_page_len"])
+        if slot_events is not None:
+            slot_events[1].record(stream)
         for l in range(L):
             p, d = lay[l]["prefill"], lay[l]["decode"]
             if events is not None:
@@ -261,15 +265,21 @@ def hybrid(args, torch, gdn, workloads):
         step()
     torch.cuda.synchronize()
     evs = [[[E(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(args.steps)]
+    sevs = [[E(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        step(evs[s], sevs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     t_pf = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in range(args.steps) for l in range(L)]
     t_dc = [evs[s][l][1].elapsed_time(evs[s][l][2]) for s in range(args.steps) for l in range(L)]
+    t_sl = [sevs[s][0].elapsed_time(sevs[s][1]) for s in range(args.steps)]
     t_pf_ms = sum(t_pf) / len(t_pf)
     t_dc_ms = sum(t_dc) / len(t_dc)
+
+    def pct(xs):
+        xs = sorted(xs)
+        return [xs[min(len(xs) - 1, int(q * len(xs)))] for q in (0.1, 0.5, 0.9)]
     ms_step = wall * 1000 / args.steps
 
     n_state_io = sum(1 for r in pre0["read_rows"] if r >= 0)
@@ -318,6 +328,8 @@ def hybrid(args, torch, gdn, workloads):
         "decode_state_GBps": dc_gbps,
         "decode_frac_hbm_peak": dc_gbps / HBM_PEAK_GBPS,
         "prefill_ms_per_layer": t_pf_ms, "decode_ms_per_layer": t_dc_ms,
+        "prefill_ms_p10_p50_p90": pct(t_pf), "decode_ms_p10_p50_p90": pct(t_dc),
+        "slots_ms_per_step": sum(t_sl) / len(t_sl),
         "roofline": roof,
     }
     if not args.no_side:
