@@ -1042,29 +1042,70 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 
 // Launch plan, one workgroup: the longest-first order of the sequences (by
 // chunk count; ties by index), the chunk-slot table and the zero row that
-// padding rows read.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu,
-                                                    const int32_t* __restrict__ prefix,
-                                                    const int32_t* __restrict__ chunk_start, int B,
-                                                    int nslots, int32_t* __restrict__ order,
-                                                    int4* __restrict__ tab,
-                                                    uint32_t* __restrict__ zero_row) {
-  if (threadIdx.x < 64) zero_row[threadIdx.x] = 0u;
-  for (int c = threadIdx.x; c < nslots; c += blockDim.x) tab[c] = int4{-1, 0, 0, 0};
-  __syncthreads();
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int pre = prefix[b];
-    const int L = cu[b + 1] - cu[b];
-    const int nb = chunks_of(pre, L);
-    int rank = 0;
-    for (int o = 0; o < B; ++o) {
-      const int no = chunks_of(prefix[o], cu[o + 1] - cu[o]);
-      rank += (no > nb) || (no == nb && o < b);
+// padding rows read.  Sequences are staged through LDS a tile at a time: the
+// rank of a sequence counts the longer (or equally long, earlier) ones tile by
+// tile, and each chunk slot finds its sequence by binary search over the
+// tile's chunk starts (ascending: an exclusive scan of the chunk counts).
+constexpr int kPlanTile = 1024;
+struct PlanSmem {
+  int cnt[kPlanTile];     // chunk count
+  int cs[kPlanTile + 1];  // first chunk slot; cs[n] = the tile's end
+  int len[kPlanTile];     // new tokens
+  int tok0[kPlanTile];    // first token
+  int nbase[kPlanTile];   // new-token index of chunk 0's row 0
+};
+
+__global__ __launch_bounds__(kPlanTile) void plan_kernel(const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ prefix,
+                                                         const int32_t* __restrict__ chunk_start, int B,
+                                                         int nslots, int32_t* __restrict__ order,
+                                                         int4* __restrict__ tab,
+                                                         uint32_t* __restrict__ zero_row) {
+  __shared__ PlanSmem sm;
+  const int tid = threadIdx.x;
+  if (tid < 64) zero_row[tid] = 0u;
+  for (int c = tid; c < nslots; c += kPlanTile) tab[c] = int4{-1, 0, 0, 0};
+  int my_cnt = 0, my_rank = 0;  // of sequence base + tid, for the tile being ranked
+  for (int base = 0; base < B; base += kPlanTile) {
+    const int b = base + tid;
+    if (b < B) my_cnt = chunks_of(prefix[b], cu[b + 1] - cu[b]);
+    my_rank = 0;
+    for (int t0 = 0; t0 < B; t0 += kPlanTile) {
+      const int n = min(kPlanTile, B - t0);
+      __syncthreads();
+      if (tid < n) {
+        const int o = t0 + tid;
+        const int pre = prefix[o], L = cu[o + 1] - cu[o];
+        sm.cnt[tid] = chunks_of(pre, L);
+        sm.cs[tid] = chunk_start[o];
+        sm.len[tid] = L;
+        sm.tok0[tid] = cu[o];
+        sm.nbase[tid] = (pre & ~(kChunk - 1)) - pre;
+        if (tid == n - 1) sm.cs[n] = chunk_start[o] + sm.cnt[tid];
+      }
+      __syncthreads();
+      if (b < B) {
+        for (int i = 0; i < n; ++i) {
+          const int no = sm.cnt[i];
+          my_rank += (no > my_cnt) || (no == my_cnt && t0 + i < b);
+        }
+      }
+      // the table for this tile's chunks, once (during the first rank pass)
+      if (base == 0) {
+        const int c0 = max(sm.cs[0], 0), c1 = min(sm.cs[n], nslots);
+        for (int c = c0 + tid; c < c1; c += kPlanTile) {
+          int lo = 0, hi = n;  // last i with cs[i] <= c
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sm.cs[mid] <= c) lo = mid;
+            else hi = mid;
+          }
+          const int j = c - sm.cs[lo];
+          if (j >= 0 && j < sm.cnt[lo]) tab[c] = int4{t0 + lo, sm.nbase[lo] + kChunk * j, sm.len[lo], sm.tok0[lo]};
+        }
+      }
     }
-    order[rank] = b;
-    const int cs = chunk_start[b];
-    const int n0 = (pre & ~(kChunk - 1)) - pre;
-    for (int j = 0; j < nb && cs + j < nslots; ++j) tab[cs + j] = int4{b, n0 + kChunk * j, L, cu[b]};
+    if (b < B) order[my_rank] = b;
   }
 }
 
@@ -1235,7 +1276,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
   if (p.split_m > 0 && (p.seg_cap1 <= 0 || p.seg_cap2 <= 0)) return hipErrorInvalidValue;
-  plan_kernel<<<1, 1024, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs,
+  plan_kernel<<<1, kPlanTile, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs,
                                  p.num_chunk_slots, p.order, p.chunk_tab, (uint32_t*)p.zero_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

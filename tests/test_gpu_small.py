@@ -130,6 +130,20 @@ def test_prefill_ragged(prefix, new):
     check_paged_prefill(pre, pool)
 
 
+def test_prefill_many_sequences():
+    """More sequences than one planning tile (1024): the longest-first ranks
+    across tiles, each chunk slot found in its tile, zero-length sequences
+    (one page, prefix only) among them."""
+    rng = np.random.default_rng(21)
+    B = 1300
+    new = rng.integers(0, 40, size=B)
+    new[::7] = 0
+    prefix = rng.integers(0, 200, size=B)
+    prefix[new == 0] += 1  # every sequence holds at least one token
+    pre, pool = make_case(prefix.tolist(), new.tolist(), H=1, Hqk=1, seed=21)
+    check_paged_prefill(pre, pool)
+
+
 def test_prefill_low_decay_gqa():
     # slow decay keeps the prefix state alive across chunks; 4 v-heads on 2 q/k heads
     pre, pool = make_case([70, 0, 300], [400, 333, 129], H=4, Hqk=2, seed=3, g_scale=0.1)
