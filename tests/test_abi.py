@@ -54,11 +54,11 @@ def test_workspace_size(lib, monkeypatch):
     a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
     b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
     c = lib.gdn_prefill_workspace_size(64 * 100, 300, C.byref(d))
-    # rows + launch order per sequence, and one 13 KiB intra-chunk record per
+    # rows + launch order per sequence, and one 11 KiB intra-chunk record per
     # (chunk slot, v-head) with at most T/64 + 2B + 1 chunk slots
     assert 0 < a < b < c
     assert a % 256 == 0 and b % 256 == 0
-    # T record (6 fragments, hi and lo) + scalars per (slot, head), and a
+    # T record (5 fragments, hi and lo) + scalars per (slot, head), and a
     # 16-byte chunk-table entry per slot (regions rounded up to 256 bytes)
     al = lambda x: (x + 255) // 256 * 256
     assert b - a == 100 * 4 * (10240 + 1024) + al(103 * 16) - al(3 * 16)
