@@ -376,14 +376,36 @@ def single(args, torch, gdn, workloads):
         H, Hqk = c["H"], c["Hqk"]
         B = int(d["last_page_len"].shape[0])
         o = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
-        sl = gdn.decode_slots(d["page_indices"], d["page_indptr"], d["last_page_len"])
+        # Four page-table variants whose touched pages (the last two of every
+        # sequence) are disjoint, used in turn, so that the 256 MB Infinity
+        # Cache cannot serve rows the previous call just wrote.
+        idx, ip = d["page_indices"], d["page_indptr"]
+        n_pages = int(c["pool"].shape[0])
+        ends = ip[1:].long()
+        pos = torch.cat([ends - 1, (ends - 2)[ends - 2 >= ip[:-1].long()]])
+        used = torch.unique(idx[pos].long())
+        free_mask = torch.ones(n_pages, dtype=torch.bool, device=dev)
+        free_mask[used] = False
+        free = torch.nonzero(free_mask).flatten()
+        free = free[torch.randperm(free.numel(), generator=torch.Generator().manual_seed(7)).to(dev)]
+        tables = [idx]
+        for r in range(3):
+            lut = torch.arange(n_pages, device=dev)
+            lut[used] = free[r * used.numel():(r + 1) * used.numel()]
+            t = idx.clone()
+            t[pos] = lut[idx[pos].long()].to(idx.dtype)
+            tables.append(t)
+        slot_sets = [gdn.decode_slots(t, ip, d["last_page_len"]) for t in tables]
+        turn = [0]
 
         def run():
+            r = turn[0] % len(tables)
+            turn[0] += 1
             gdn.decode_paged(d["q"], d["k"], d["v"], d["g"], d["beta"], c["pool"],
-                             d["page_indices"], d["page_indptr"], 1024, d["last_page_len"],
-                             slots=sl, out=o)
+                             tables[r], ip, 1024, d["last_page_len"], slots=slot_sets[r], out=o)
         work_bytes = decode_bytes(B, H, Hqk)
-        desc = "paged decode B=256, Hqk=16, H=32, page 1024, 25% new-page tokens"
+        desc = ("paged decode B=256, Hqk=16, H=32, page 1024, 25% new-page tokens, four page "
+                "tables with disjoint touched pages in turn")
         unit_val = lambda ms: work_bytes / (ms / 1e3) / 1e9  # noqa: E731
         unit = "decode state GB/s"
     else:
