@@ -29,7 +29,10 @@
  *
  * Calls are asynchronous on `stream`, never synchronize with the host and
  * allocate nothing: the caller passes a workspace where one is needed
- * (gdn_prefill_workspace_size).  Return value: GDN_OK or a negative status,
+ * (gdn_prefill_workspace_size).  A call only launches kernels on `stream` (no
+ * memset, copy or allocation), so it can be captured into a HIP graph and
+ * replayed; the launch decisions (tile width, sequence-parallel split) are
+ * taken on the host from the sizes at capture time.  Return value: GDN_OK or a negative status,
  * set before any launch for every check the host can make; the message is in
  * gdn_last_error() (thread-local).  Device-side contents are NOT validated
  * (the page says slots are not checked against the page table): page ids must
