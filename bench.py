@@ -459,7 +459,7 @@ def single(args, torch, gdn, workloads):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "one GPU only: the path runs on a single GPU and has no multi-GPU mode",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -61,7 +61,7 @@ extern "C" {
 enum {
   GDN_OK = 0,
   GDN_EINVAL = -1,        /* bad argument (null pointer, size, missing companion) */
-  GDN_EUNSUPPORTED = -2,  /* valid per the page but not served by this build */
+  GDN_EUNSUPPORTED = -2,  /* valid per the page but not served by this library */
   GDN_ELAUNCH = -3,       /* a kernel launch failed */
   GDN_EWORKSPACE = -4     /* workspace missing or too small */
 };
