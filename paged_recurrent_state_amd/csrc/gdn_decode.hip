@@ -12,24 +12,25 @@
 // last page in place); explicit mode takes index arrays.  A read row of -1
 // starts from literal zeros; a write row of -1 skips the store.
 //
-// Layout: one 256-thread workgroup per (sequence, head).  Each 16-lane group
+// Layout: one workgroup of NW waves per (sequence, head).  Each 16-lane group
 // owns one state row at a time: for an fp32 state (512-byte rows) lane c
 // holds k = 4c..4c+3 and 64+4c..64+4c+3, so one 16-byte load instruction
 // covers 4 whole rows; for a bf16 state (256-byte rows) lane c holds
 // k = 8c..8c+7, one 16-byte load a row.  The row's dot products reduce inside
-// the 16-lane group with 4 DPP steps (no LDS traffic).  16 rows per workgroup
-// per step, all 8 steps' loads issued before any arithmetic; the update runs
-// in fp32 either way and a bf16 row is stored rounded to nearest even.
+// the 16-lane group with 4 DPP steps (no LDS traffic).  4 NW rows per
+// workgroup per step, all 128 / (4 NW) steps' loads issued before any
+// arithmetic; the update runs in fp32 either way and a bf16 row is stored
+// rounded to nearest even.
 // Loads and stores bypass the caches' retention (non-temporal): every byte is
 // touched once.
+#include <cstdlib>
+
 #include "gdn_internal.h"
 
 namespace gdn {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kSteps = kDim / 16;  // 8: 16 rows per workgroup per step
 
 __device__ __forceinline__ int64_t ld_index(const void* p, int i, int idx64) {
   return idx64 ? ((const int64_t*)p)[i] : (int64_t)((const int32_t*)p)[i];
@@ -63,8 +64,10 @@ __device__ __forceinline__ void unpack8(u32x4 w, float* f) {
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
+template <bool BF16, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+  constexpr int kRowsPerStep = 4 * NW;
+  constexpr int kSteps = kDim / kRowsPerStep;
   const int bid = blockIdx.x;
   const int b = bid / p.H;
   const int h = bid - b * p.H;
@@ -118,12 +121,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
       const u16* src = (const u16*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 8 * c;
 #pragma unroll
       for (int it = 0; it < kSteps; ++it)
-        sb[it] = __builtin_nontemporal_load((const u32x4*)(src + (16 * it + 4 * wid + g) * kDim));
+        sb[it] = __builtin_nontemporal_load((const u32x4*)(src + (kRowsPerStep * it + 4 * wid + g) * kDim));
     } else {
       const float* src = (const float*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * c;
 #pragma unroll
       for (int it = 0; it < kSteps; ++it) {
-        const int row = 16 * it + 4 * wid + g;
+        const int row = kRowsPerStep * it + 4 * wid + g;
         s[it][0] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
         s[it][1] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim + 64));
       }
@@ -137,18 +140,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   }
   float vv[kSteps];
 #pragma unroll
-  for (int it = 0; it < kSteps; ++it) vv[it] = bf2f(p.v[bh * kDim + 16 * it + 4 * wid + g]);
+  for (int it = 0; it < kSteps; ++it) vv[it] = bf2f(p.v[bh * kDim + kRowsPerStep * it + 4 * wid + g]);
 
+  // every product-sum is an explicit fused multiply-add, so the result does
+  // not depend on how the compiler contracts a given instance
   float kq = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kq += k8[i] * q8[i];
+  for (int i = 0; i < 8; ++i) kq = __builtin_fmaf(k8[i], q8[i], kq);
   kq = sum16(kq);
 
   const int64_t doff = wr >= 0 ? wr * p.out_stride + (int64_t)h * kDim * kDim : 0;
-  float o_mine = 0.f;  // o of row 16*c + 4*wid + g (lanes c < 8)
+  float o_mine = 0.f;  // o of row kRowsPerStep*c + 4*wid + g (lanes c < kSteps)
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
-    const int row = 16 * it + 4 * wid + g;
+    const int row = kRowsPerStep * it + 4 * wid + g;
     float sv[8];  // the lane's 8 state values, in k8's order
     if constexpr (BF16) {
       unpack8(sb[it], sv);
@@ -159,15 +164,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
     float sk = 0.f, sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sk += sv[i] * k8[i];
-      sq += sv[i] * q8[i];
+      sk = __builtin_fmaf(sv[i], k8[i], sk);
+      sq = __builtin_fmaf(sv[i], q8[i], sq);
     }
     sk = sum16(sk);
     sq = sum16(sq);
-    const float delta = bt * (vv[it] - alpha * sk);
+    const float delta = bt * __builtin_fmaf(-alpha, sk, vv[it]);
     float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = alpha * sv[i] + delta * k8[i];
+    for (int i = 0; i < 8; ++i) y[i] = __builtin_fmaf(alpha, sv[i], delta * k8[i]);
     if (wr >= 0) {
       if constexpr (BF16) {
         u16* dst = (u16*)p.out + doff + 8 * c;
@@ -179,19 +184,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
         __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]}, (f32x4*)(dst + row * kDim + 64));
       }
     }
-    if (c == it) o_mine = p.scale * (alpha * sq + delta * kq);
+    if (c == it) o_mine = p.scale * __builtin_fmaf(alpha, sq, delta * kq);
   }
-  if (c < kSteps) p.o[bh * kDim + 16 * c + 4 * wid + g] = f2bf(o_mine);
+  if (c < kSteps) p.o[bh * kDim + kRowsPerStep * c + 4 * wid + g] = f2bf(o_mine);
 }
 
 }  // namespace
 
+template <int NW>
+hipError_t launch_decode_nw(const DecodeParams& p, unsigned blocks, hipStream_t s) {
+  if (p.state_bf16) decode_kernel<true, NW><<<blocks, NW * 64, 0, s>>>(p);
+  else decode_kernel<false, NW><<<blocks, NW * 64, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// Sixteen waves a workgroup (two steps of 64 rows) move the state at 5.6-5.7
+// TB/s on the hybrid step's decode batch, four waves (eight steps) at 5.4-5.5,
+// two and eight waves at 5.2-5.4.  GDN_DECODE_WAVES = 2, 4, 8 or 16 selects
+// one (tests, tuning); the results are bit-identical.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0) return hipSuccess;
-  if (p.state_bf16) decode_kernel<true><<<(unsigned)blocks, kThreads, 0, s>>>(p);
-  else decode_kernel<false><<<(unsigned)blocks, kThreads, 0, s>>>(p);
-  return hipGetLastError();
+  int nw = 16;
+  if (const char* f = getenv("GDN_DECODE_WAVES")) nw = atoi(f);
+  switch (nw) {
+    case 2: return launch_decode_nw<2>(p, (unsigned)blocks, s);
+    case 4: return launch_decode_nw<4>(p, (unsigned)blocks, s);
+    case 8: return launch_decode_nw<8>(p, (unsigned)blocks, s);
+    default: return launch_decode_nw<16>(p, (unsigned)blocks, s);
+  }
 }
 
 }  // namespace gdn

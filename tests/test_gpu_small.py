@@ -224,6 +224,36 @@ def test_decode_paths_agree_and_match_oracle():
         check_state(pool[r], s)
 
 
+@pytest.mark.parametrize("waves", ["2", "4", "8", "16"])
+def test_decode_every_workgroup_width(waves):
+    """Each decode workgroup shape (2, 4, 8 or 16 waves, 64 / 32 / 16 / 8 rows
+    a wave) against the oracle, fp32 and bf16 pools, GQA and new-page rows."""
+    m = lib()
+    os.environ["GDN_DECODE_WAVES"] = waves
+    try:
+        c = cuda(workloads.config2(num_seqs=12, qk_heads=2, v_heads=4, num_pages=12 * 32,
+                                   new_page_seqs=4, seed=40 + int(waves)))
+        dec = c["decode"]
+        for pool in (c["pool"], c["pool"].to(torch.bfloat16)):
+            rows_in = pool_rows_cpu(pool, dec["read_rows"])
+            before = pool.clone()
+            o = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
+                               dec["page_indices"], dec["page_indptr"], 1024, dec["last_page_len"])
+            torch.cuda.synchronize()
+            o_ref, writes, _ = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
+                                                 dec["g"].cpu(), dec["beta"].cpu(),
+                                                 RowView(rows_in), dec["page_indices"].cpu(),
+                                                 dec["page_indptr"].cpu(),
+                                                 dec["last_page_len"].cpu(),
+                                                 state_dtype=state_dtype_of(pool))
+            check_outputs(o, o_ref)
+            assert changed_rows(before, pool) == sorted(writes)
+            for r, s in writes.items():
+                check_state(pool[r], s)
+    finally:
+        del os.environ["GDN_DECODE_WAVES"]
+
+
 @pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
 def test_general_decode_rows(idx_dtype):
     m = lib()
