@@ -58,3 +58,84 @@ def test_random_paged_prefill(seed):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+
+
+def draw_general(seed):
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 6))
+    H, Hqk = [(1, 1), (2, 1), (2, 2), (4, 2)][int(rng.integers(0, 4))]
+    N = int(rng.choice([1, 17, 48, 64, 100, 128, 200]))
+    max_len = 40 if N == 1 else (120 if N < 64 else 300)
+    special = [0, 1, 63, 64, 65, N - 1, N, N + 1]
+    prefix = [int(rng.choice(special)) if rng.random() < 0.4 else int(rng.integers(0, 500))
+              for _ in range(B)]
+    new = [min(max_len, int(rng.choice(special)) if rng.random() < 0.4
+               else int(rng.integers(0, max_len + 1))) for _ in range(B)]
+    return dict(B=B, H=H, Hqk=Hqk, N=N, prefix=[max(0, x) for x in prefix],
+                new=[max(0, x) for x in new], g_scale=float(rng.choice([0.1, 1.0])),
+                bf16=bool(rng.random() < 0.3), idx64=bool(rng.random() < 0.5),
+                scale=None if rng.random() < 0.7 else 0.05, rng=rng)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_general_prefill(seed):
+    """The slot-argument call with three separate state buffers, random -1
+    rows (zero start, skipped final or checkpoint store), int32 or int64 rows,
+    any checkpoint interval and an explicit scale, against the oracle; every
+    row no sequence writes keeps its NaN bits."""
+    import torch
+
+    import workloads
+    from oracle import gdn as ogdn
+    from tests.gpu_util import RowView, changed_rows, check_outputs, check_state, pool_rows_cpu
+    from tests.test_gpu_small import lib
+
+    m = lib()
+    c = draw_general(seed)
+    rng, B, H, Hqk, N = c["rng"], c["B"], c["H"], c["Hqk"], c["N"]
+    dev = "cuda"
+    gen = workloads.generator(seed)
+    T = sum(c["new"])
+    t = {k: v.to(dev) for k, v in workloads.token_inputs(T, Hqk, H, 128, 128, gen,
+                                                          g_scale=c["g_scale"]).items()}
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(c["new"])]), dtype=torch.int32, device=dev)
+    n_ck = [(p + n) // N - p // N for p, n in zip(c["prefix"], c["new"])]
+    ck_start = np.concatenate([[0], np.cumsum(n_ck)])[:-1]
+    R_in, R_out, R_ck = B + 2, B + 2, max(1, sum(n_ck) + 2)
+    sidx = [int(x) if rng.random() < 0.7 else -1 for x in rng.permutation(R_in)[:B]]
+    oidx = [int(x) if rng.random() < 0.8 else -1 for x in rng.permutation(R_out)[:B]]
+    cidx = [int(x) if rng.random() < 0.7 else -1 for x in rng.permutation(R_ck)[:sum(n_ck)]]
+    sd = torch.bfloat16 if c["bf16"] else torch.float32
+    init = workloads.nan_pool(R_in, H, 128, 128, device=dev)
+    workloads.fill_rows(init, [r for r in sidx if r >= 0], workloads.gen_on(seed + 7, dev), 0.09)
+    init = init.to(sd)
+    out = workloads.nan_pool(R_out, H, 128, 128, device=dev).to(sd)
+    ck = workloads.nan_pool(R_ck, H, 128, 128, device=dev).to(sd)
+    it = torch.int64 if c["idx64"] else torch.int32
+    mk = lambda x: torch.tensor(np.asarray(x, dtype=np.int64), dtype=it, device=dev)  # noqa: E731
+    rows_in = pool_rows_cpu(init, [r for r in sidx if r >= 0])
+    out0, ck0 = out.clone(), ck.clone()
+    o = m.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, initial_state=init,
+                  state_indices=mk(sidx), output_state=out, output_state_indices=mk(oidx),
+                  output_final_state=True, state_checkpoints=ck,
+                  checkpoint_state_indices=mk(cidx if cidx else [0]),
+                  checkpoint_cu_starts=mk(ck_start), prefix_lens=mk(c["prefix"]),
+                  checkpoint_every_n_tokens=N, scale=c["scale"])
+    torch.cuda.synchronize()
+    res = ogdn.prefill(t["q"].cpu(), t["k"].cpu(), t["v"].cpu(), t["g"].cpu(), t["beta"].cpu(),
+                       cu.cpu(), initial_state=RowView(rows_in), state_indices=sidx,
+                       output_final_state=True, output_state_indices=oidx,
+                       checkpoint_state_indices=cidx if cidx else [0],
+                       checkpoint_cu_starts=list(ck_start), prefix_lens=c["prefix"],
+                       checkpoint_every_n_tokens=N, scale=c["scale"], shared_pool=False,
+                       state_dtype="bf16" if c["bf16"] else "fp32")
+    if T:
+        check_outputs(o, res.o)
+    assert changed_rows(out0, out) == sorted(res.final)
+    assert changed_rows(ck0, ck) == sorted(res.checkpoints)
+    for r, s in res.final.items():
+        check_state(out[r], s, f"final row {r}")
+    for r, s in res.checkpoints.items():
+        check_state(ck[r], s, f"checkpoint row {r}")
+    print(f"general case {seed}: B={B} H={H}/{Hqk} N={N} prefix={c['prefix']} new={c['new']} "
+          f"finals={len(res.final)} checkpoints={len(res.checkpoints)}")
