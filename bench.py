@@ -195,6 +195,10 @@ def side_measurements(torch, gdn, workloads, pool, dec, ps, H, Hqk, t_dc_ms):
         "ms": ms, "state_GBps": by / (ms / 1e3) / 1e9,
         "frac_hbm_peak": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "fp32_pool_ms": t_dc_ms}
     c = workloads.config3(device=dev)
+    # one workspace for the largest call serves every call (sizes only grow)
+    t_max = max(int(call["q"].shape[0]) for call in c["calls"])
+    ws = torch.empty(gdn.prefill_workspace_size(t_max, 1, c["H"], c["Hqk"]), dtype=torch.uint8,
+                     device=dev)
 
     def run():
         for call in c["calls"]:
@@ -205,7 +209,8 @@ def side_measurements(torch, gdn, workloads, pool, dec, ps, H, Hqk, t_dc_ms):
                         output_final_state=True, state_checkpoints=c["state_checkpoints"],
                         checkpoint_state_indices=c["checkpoint_state_indices"],
                         checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                        prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=c["every_n"])
+                        prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=c["every_n"],
+                        workspace=ws)
     T = sum(int(call["q"].shape[0]) for call in c["calls"])
     ms_split = _median_ms(torch, run, 5)
     os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = "0"

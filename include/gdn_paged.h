@@ -137,8 +137,10 @@ int gdn_decode_slots(const int32_t* page_indices, const int32_t* page_indptr,
 
 /*
  * Workspace bytes gdn_prefill_paged / gdn_prefill need for a batch of
- * `total_tokens` new tokens in `num_seqs` sequences (an upper bound that
- * depends on sizes only, so it can be sized once).  0 on bad dims.
+ * `total_tokens` new tokens in `num_seqs` sequences: an upper bound that
+ * depends on sizes only and never decreases as either grows, so a workspace
+ * sized for the largest call serves every call with at most as many tokens
+ * and sequences.  0 on bad dims.
  * Batches whose (sequence, v-head) pairs leave most of the GPU idle (B * H <=
  * 64) and whose sequences are long run the recurrence sequence-parallel:
  * every sequence is cut into segments, each segment's transition S -> S M +

@@ -65,8 +65,14 @@ struct WsLayout {
 // G - 1 scan steps.  G = 256 / n fills the second pass once, and the split
 // wins by about G / 3: only when n <= 64 and the sequences are long.
 // GDN_PREFILL_SPLIT_CHUNKS = m forces segments of m chunks (0: never split).
+// GDN_PREFILL_SPLIT_CHUNKS as set (m >= 0), or -1 when it is not
+int forced_split() {
+  const char* f = getenv("GDN_PREFILL_SPLIT_CHUNKS");
+  return f ? std::max(0, atoi(f)) : -1;
+}
+
 int split_chunks(int64_t T, int B, int H) {
-  if (const char* f = getenv("GDN_PREFILL_SPLIT_CHUNKS")) return std::max(0, atoi(f));
+  if (const int m = forced_split(); m >= 0) return m;
   const int64_t n = (int64_t)B * H;
   if (B <= 0 || n > 64) return 0;
   const int64_t nc = T / kChunk + 2 * (int64_t)B;
@@ -75,12 +81,30 @@ int split_chunks(int64_t T, int B, int H) {
   return (int)std::max<int64_t>(4, (nc + B * G - 1) / (B * G));
 }
 
-WsLayout ws_layout(int64_t T, int B, int H) {
+// Workspace regions for a call of T tokens in B sequences.  With `bound`,
+// the sequence-parallel regions are sized for every call of at most T tokens
+// and B sequences (the size query: one workspace serves every smaller call);
+// without, for this call's own segments (the layout a call uses).
+WsLayout ws_layout(int64_t T, int B, int H, bool bound = false) {
   WsLayout w;
   w.nc = T / kChunk + 2 * (int64_t)B + 1;
   w.split_m = split_chunks(T, B, H);
   // a sequence of c chunks has ceil(c / m) <= c / m + 1 segments
-  const int64_t segs = w.split_m > 0 ? w.nc / w.split_m + B : 0;
+  int64_t segs = w.split_m > 0 ? w.nc / w.split_m + B : 0;
+  if (bound && forced_split() < 0 && H <= 64) {
+    // A call of T' <= T tokens in B' <= B sequences splits only when B' H <=
+    // 64 and T' / 64 >= 14 B'.  Its m is at least 4 and at least nc' / (B' G')
+    // with G' = 256 / (B' H), so it has at most (nc' + 1) / m + B' segments:
+    // <= B' G' (1 + 1/16) + B' and <= (T / 64 + 2 B' + 1) / 4 + B'.  Both
+    // bounds grow with T and B, so the size does too.
+    const int64_t bmax = std::min<int64_t>({(int64_t)B, 64 / H, T / (14 * kChunk)});
+    if (bmax >= 1) {
+      const int64_t G1 = 256 / H;
+      const int64_t by_g = G1 + G1 / 16 + 1 + bmax;
+      const int64_t by_t = (T / kChunk + 2 * bmax + 1) / 4 + bmax;
+      segs = std::max(segs, std::min(by_g, by_t));
+    }
+  }
   w.cap1 = 2 * segs;
   w.cap2 = segs;
   w.rows = 3 * segs;
@@ -98,7 +122,7 @@ WsLayout ws_layout(int64_t T, int B, int H) {
   w.scal = off;
   off += align256((size_t)w.nc * H * kRecScal * sizeof(float));
   w.seg1 = w.seg2 = w.scan = w.counts = w.states = off;
-  if (w.split_m > 0) {
+  if (segs > 0) {
     w.seg1 = off;
     off += align256((size_t)w.cap1 * kSegWords * sizeof(int32_t));
     w.seg2 = off;
@@ -217,7 +241,7 @@ const char* gdn_version(void) { return "gdn_paged 0.1.0 (gfx950)"; }
 
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, const gdn_dims_t* dims) {
   if (check_dims(dims) != GDN_OK || total_tokens < 0 || num_seqs < 0) return 0;
-  return ws_layout(total_tokens, num_seqs, dims->num_v_heads).total;
+  return ws_layout(total_tokens, num_seqs, dims->num_v_heads, true).total;
 }
 
 int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,

@@ -80,15 +80,37 @@ def test_workspace_size_sequence_parallel(lib, monkeypatch):
         extra = al(2 * segs * 32) + al(segs * 32) + al(16) + 256 + 3 * segs * 4 * 128 * 128 * 4
         assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == extra
     monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS")
-    # default: ~512 / H segments in all, at least 4 chunks each -> m = 4 here
+    # default: room for the segments of ANY call of at most these sizes, the
+    # smaller of 256/H + 256/H/16 + 1 + B' = 70 and (T/64 + 2B' + 1)/4 + B' = 26
+    # (B' = min(B, 64/H, T/896) = 1): m = 4 here
     assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == \
         al(52 * 32) + al(26 * 32) + al(16) + 256 + 78 * 4 * 128 * 128 * 4
-    # enough (sequence, head) pairs to fill the chip: no split
+    # a batch that fills the chip does not split itself, but a smaller one
+    # within the same sizes may: min(256/32 + 0 + 1 + 2, 1005/4 + 2) = 11 segments
     big = dims(H=32, Hqk=32)
     monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")
     w0 = lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big))
     monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS")
-    assert lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big)) == w0
+    assert lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big)) - w0 == \
+        al(22 * 32) + al(11 * 32) + al(8 * 16) + 256 + 33 * 32 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("H", [1, 4, 32, 128])
+def test_workspace_size_monotone(lib, monkeypatch, H):
+    """A workspace sized for (T, B) serves every call with fewer tokens or
+    sequences: the size never drops as either grows (the sequence-parallel
+    choice depends on both)."""
+    monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS", raising=False)
+    d = dims(H=H, Hqk=1)
+    size = lambda T, B: lib.gdn_prefill_workspace_size(T, B, C.byref(d))  # noqa: E731
+    Ts = [0, 1, 63, 64, 65, 640, 1000, 1024, 4000, 8191, 8192, 30000, 70000, 200000]
+    Bs = [1, 2, 3, 7, 16, 64, 65, 300]
+    for B in Bs:
+        sizes = [size(T, B) for T in Ts]
+        assert sizes == sorted(sizes), (H, B, sizes)
+    for T in Ts:
+        sizes = [size(T, B) for B in Bs]
+        assert sizes == sorted(sizes), (H, T, sizes)
 
 
 def _prefill_paged(lib, d, page_size=128, stride=4 * 128 * 128, ws=1 << 30, pool=1, cu=1,
