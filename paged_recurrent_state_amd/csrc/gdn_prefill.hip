@@ -23,8 +23,9 @@
 //   mask, and T by forward substitution in fp32 on the 16x16 diagonal blocks
 //   plus a two-level doubling on MFMA (hi/lo bf16 splits) for the
 //   off-diagonal blocks.  T diag(beta) leaves as ready-to-load MFMA fragments
-//   (hi and lo bf16 halves, the all-zero ones dropped), with the per-row
-//   scalars beta, G, gamma and exp(G_last - G).
+//   (hi and lo bf16 halves; the all-zero ones dropped, the two half-empty
+//   ones packed into one), with the per-row scalars beta, G, gamma and
+//   exp(G_last - G).
 // rec_kernel (one workgroup per (sequence, v-head), longest sequences first):
 //   walks the chunks in order.  Per chunk, the P = D * (Q K^T) fragments come
 //   straight out of MFMA accumulators (computed as P^T blocks), K^T fragments
