@@ -1180,15 +1180,28 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const PrefillParams p)
 // next one lands while this one multiplies); the current rows stay in LDS.
 // Thread (r, c) owns row r and the columns 4c .. 4c+3 and 64+4c .. 64+4c+3,
 // so a 16-lane group's 16-byte reads of an M row cover all 64 banks.
+// M_g as row pairs (2 x 128 floats, one global-to-LDS load each) 16 bytes
+// apart from the next pair, so that the four lane groups of an operand read
+// (rows 8 apart) fall in different banks; double-buffered by step parity.
+constexpr int kPairPitch = 2 * kDim + 4;
 struct ScanSmem {
-  float M[2][kDim][kDim];
-  float S[16][kDim];
+  float M[2][kDim / 2][kPairPitch];
+  float S[16][kDim + 4];  // the workgroup's 16 rows of start_g
 };
 
+// Workgroup (sequence, v-head, rb) composes rows 16 rb .. 16 rb + 15 of the
+// segment start states: start_{g+1} = start_g M_g + N_g, g = 0 .. G - 2.  The
+// product runs on MFMA with fp32 operands split hi/lo (3 passes, ~2^-16
+// relative): wave w produces columns 32 w .. 32 w + 31 (two 16 x 16 tiles),
+// the output's lane (n, q) holding rows 4q .. 4q + 3 of column n.  The 8
+// workgroups of a (sequence, v-head) sit 8 block indices apart -- the same
+// XCD -- so that 7 of the 8 reads of each M_g hit in that XCD's L2.
 __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
-  const int rb = blockIdx.x & 7, bh = blockIdx.x >> 3;
+  const int j = blockIdx.x;
+  const int rb = (j >> 3) & 7, bh = 8 * (j >> 6) + (j & 7);
+  if (bh >= p.num_seqs * p.H) return;  // the last group of 8 heads may be partial
   const int b = bh / p.H, h = bh - b * p.H;
   const int4 sc = p.seg_scan[b];
   const int G = sc.x, row0 = sc.y;
@@ -1196,17 +1209,18 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   const int rd = p.slots.read[b];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, gq = lane >> 4;
   const int r = tid >> 4, c0 = 4 * (tid & 15);
   const int64_t hoff = (int64_t)h * kDim * kDim;
   auto state = [&](int row) { return p.ws_state + (int64_t)row * p.ws_state_stride + hoff; };
-  // M_g into buffer X: 64 blocks of 1 KiB (2 rows each), 16 per wave
+  // M_g into buffer X: 64 row pairs of 1 KiB, 16 per wave
   auto fetch = [&](int g, int X) {
     const char* src = uniform_ptr(state(row0 + 2 * (G - 1) + g));
     const uint32_t dst = lds_addr(&sm.M[X][0][0]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int blk = 16 * wid + i;
-      lds_load16_at(dst + blk * 1024, src + blk * 1024, lane * 16);
+      lds_load16_at(dst + blk * (kPairPitch * 4), src + blk * 1024, lane * 16);
     }
   };
   fetch(0, 0);
@@ -1234,25 +1248,49 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   for (int g = 0; g <= G - 2; ++g) {
     const int X = g & 1;
     if (g + 1 <= G - 2) fetch(g + 1, X ^ 1);
-    const float* Ng = state(row0 + G - 1 + g) + (int64_t)(16 * rb + r) * kDim;
-    f32x4 a0 = *(const f32x4*)(Ng + c0), a1 = *(const f32x4*)(Ng + 64 + c0);
-#pragma unroll 8
-    for (int i = 0; i < kDim; ++i) {
-      const float sv = sm.S[r][i];
-      const f32x4 m0 = *(const f32x4*)&sm.M[X][i][c0];
-      const f32x4 m1 = *(const f32x4*)&sm.M[X][i][64 + c0];
+    // this lane's outputs: rows 4 gq + i, columns 32 wid + 16 t + n16; N_g is
+    // added after the product, so its loads are in flight meanwhile
+    const float* Ng = state(row0 + G - 1 + g) + (int64_t)(16 * rb) * kDim + 32 * wid + n16;
+    float nv[2][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a0[e] = fmaf(sv, m0[e], a0[e]);
-        a1[e] = fmaf(sv, m1[e], a1[e]);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nv[t][i] = Ng[(4 * gq + i) * kDim + 16 * t];
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks + 8 * gq;  // this lane's 8 k of the step
+      float av[8];
+      *(f32x4*)&av[0] = *(const f32x4*)&sm.S[n16][k0];
+      *(f32x4*)&av[4] = *(const f32x4*)&sm.S[n16][k0 + 4];
+      bf16x8 ahi, alo;
+      split8(av, ahi, alo);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int n = 32 * wid + 16 * t + n16;
+        float bv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = sm.M[X][(k0 + j) >> 1][((k0 + j) & 1) * kDim + n];
+        bf16x8 bhi, blo;
+        split8(bv, bhi, blo);
+        acc[t] = mfma16x16x32(ahi, bhi, acc[t]);
+        acc[t] = mfma16x16x32(ahi, blo, acc[t]);
+        acc[t] = mfma16x16x32(alo, bhi, acc[t]);
       }
     }
-    float* out = state(row0 + g) + (int64_t)(16 * rb + r) * kDim;  // start_{g+1}
-    *(f32x4*)(out + c0) = a0;
-    *(f32x4*)(out + 64 + c0) = a1;
-    __syncthreads();  // every thread is done reading S and M[X]
-    *(f32x4*)&sm.S[r][c0] = a0;
-    *(f32x4*)&sm.S[r][64 + c0] = a1;
+    float* out = state(row0 + g) + (int64_t)(16 * rb) * kDim + 32 * wid + n16;  // start_{g+1}
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[t][i] += nv[t][i];
+        out[(4 * gq + i) * kDim + 16 * t] = acc[t][i];
+      }
+    __syncthreads();  // every wave is done reading S and M[X]
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.S[4 * gq + i][32 * wid + 16 * t + n16] = acc[t][i];
     wait_loads();     // this wave's part of the next M has landed
     __syncthreads();  // ... and every wave's; the new rows are in place
   }
@@ -1324,7 +1362,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
       attr_set = true;
     }
   }
-  seg_scan_kernel<<<(unsigned)((int64_t)p.num_seqs * p.H * 8), 256, sizeof(ScanSmem), s>>>(p);
+  seg_scan_kernel<<<(unsigned)(((int64_t)p.num_seqs * p.H + 7) / 8 * 64), 256, sizeof(ScanSmem), s>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   PrefillParams p2 = p;
   p2.vseq = p.seg2;
