@@ -1056,12 +1056,10 @@ struct PlanSmem {
   int nbase[kPlanTile];   // new-token index of chunk 0's row 0
 };
 
-__global__ __launch_bounds__(kPlanTile) void plan_kernel(const int32_t* __restrict__ cu,
-                                                         const int32_t* __restrict__ prefix,
-                                                         const int32_t* __restrict__ chunk_start, int B,
-                                                         int nslots, int32_t* __restrict__ order,
-                                                         int4* __restrict__ tab,
-                                                         uint32_t* __restrict__ zero_row) {
+__device__ void plan_body(const int32_t* __restrict__ cu, const int32_t* __restrict__ prefix,
+                          const int32_t* __restrict__ chunk_start, int B, int nslots,
+                          int32_t* __restrict__ order, int4* __restrict__ tab,
+                          uint32_t* __restrict__ zero_row) {
   __shared__ PlanSmem sm;
   const int tid = threadIdx.x;
   if (tid < 64) zero_row[tid] = 0u;
@@ -1122,7 +1120,7 @@ __global__ __launch_bounds__(kPlanTile) void plan_kernel(const int32_t* __restri
 //                row), the last one writing the final state.
 // Workspace state rows of b, from row0: start_1 .. start_{G-1}, then
 // N_0 .. N_{G-2}, then M_0 .. M_{G-2}.
-__global__ __launch_bounds__(1024) void split_plan_kernel(const PrefillParams p) {
+__device__ void split_plan(const PrefillParams& p) {
   const int m = p.split_m, B = p.num_seqs;
   int carry1 = 0, carry2 = 0, carry_row = 0;
   for (int base = 0; base < B; base += blockDim.x) {
@@ -1173,13 +1171,20 @@ __global__ __launch_bounds__(1024) void split_plan_kernel(const PrefillParams p)
   }
 }
 
-// start_{g+1} = start_g M_g + N_g for g = 0 .. G-2, fp32, 16 state rows of
-// one (sequence, v-head) per workgroup: rows of a state evolve independently,
-// so the 8 row blocks of a head run in parallel.  The transitions M_g (64 KiB
+// The launch plan, and with the sequence-parallel recurrence its segment
+// plan too (the two read the slot rows only, not each other's output): one
+// workgroup of kPlanTile threads, one launch.
+__global__ __launch_bounds__(kPlanTile) void plan_kernel(const PrefillParams p) {
+  plan_body(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs, p.num_chunk_slots,
+            p.order, p.chunk_tab, (uint32_t*)p.zero_row);
+  if (p.split_m > 0) split_plan(p);
+}
+
+// start_{g+1} = start_g M_g + N_g for g = 0 .. G-2, 16 state rows of one
+// (sequence, v-head) per workgroup: rows of a state evolve independently, so
+// the 8 row blocks of a head run in parallel.  The transitions M_g (64 KiB
 // each) stream into LDS straight from global memory, double-buffered (the
 // next one lands while this one multiplies); the current rows stay in LDS.
-// Thread (r, c) owns row r and the columns 4c .. 4c+3 and 64+4c .. 64+4c+3,
-// so a 16-lane group's 16-byte reads of an M row cover all 64 banks.
 // M_g as row pairs (2 x 128 floats, one global-to-LDS load each) 16 bytes
 // apart from the next pair, so that the four lane groups of an operand read
 // (rows 8 apart) fall in different banks; double-buffered by step parity.
@@ -1315,8 +1320,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
   if (p.split_m > 0 && (p.seg_cap1 <= 0 || p.seg_cap2 <= 0)) return hipErrorInvalidValue;
-  plan_kernel<<<1, kPlanTile, 0, s>>>(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs,
-                                 p.num_chunk_slots, p.order, p.chunk_tab, (uint32_t*)p.zero_row);
+  plan_kernel<<<1, kPlanTile, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   wy_kernel<<<(unsigned)(num_chunk_slots * p.H), kWyThreads, 0, s>>>(p);
@@ -1346,9 +1350,8 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
     }
   };
   if (p.split_m <= 0) return rec(p, p.num_seqs, true);
-  // sequence-parallel: plan, first pass, scan of the segment maps, second pass
-  split_plan_kernel<<<1, 1024, 0, s>>>(p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // sequence-parallel (its segment plan came with the launch plan): first
+  // pass, scan of the segment maps, second pass
   PrefillParams p1 = p;
   p1.vseq = p.seg1;
   p1.vcount = p.seg_counts;
