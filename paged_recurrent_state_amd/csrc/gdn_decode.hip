@@ -23,6 +23,7 @@
 // rounded to nearest even.
 // Loads and stores bypass the caches' retention (non-temporal): every byte is
 // touched once.
+#include <algorithm>
 #include <cstdlib>
 
 #include "gdn_internal.h"
@@ -64,115 +65,124 @@ __device__ __forceinline__ void unpack8(u32x4 w, float* f) {
   }
 }
 
-template <bool BF16, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
-  constexpr int kRowsPerStep = 4 * NW;
-  constexpr int kSteps = kDim / kRowsPerStep;
-  const int bid = blockIdx.x;
-  const int b = bid / p.H;
-  const int h = bid - b * p.H;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int g = lane >> 4;  // row within the wave's 4 rows of a step
-  const int c = lane & 15;  // k = 4c..4c+3 and 64+4c..64+4c+3 (fp32), 8c..8c+7 (bf16)
-
+// Rows of sequence b: paged mode derives them from the page table; explicit
+// mode takes index arrays (null: row b, and the write row = the read row).
+struct DecRows {
   int64_t rd, wr;
+};
+__device__ __forceinline__ DecRows decode_rows(const DecodeParams& p, int b) {
   if (p.mode == 1) {
     const int end = p.page_indptr[b + 1];
     const int last = p.page_indices[end - 1];
-    wr = last;
-    rd = p.last_page_len[b] == 1 ? p.page_indices[end - 2] : last;
-  } else {
-    const int64_t r0 = p.rd_idx ? ld_index(p.rd_idx, b, p.idx64) : (int64_t)b;
-    rd = p.init ? r0 : -1;
-    wr = p.out ? (p.wr_idx ? ld_index(p.wr_idx, b, p.idx64) : r0) : -1;
+    return DecRows{p.last_page_len[b] == 1 ? p.page_indices[end - 2] : last, last};
   }
+  const int64_t r0 = p.rd_idx ? ld_index(p.rd_idx, b, p.idx64) : (int64_t)b;
+  return DecRows{p.init ? r0 : -1, p.out ? (p.wr_idx ? ld_index(p.wr_idx, b, p.idx64) : r0) : -1};
+}
 
+// What a lane holds of one (sequence, v-head): its state values (step it
+// covers rows kRowsPerStep * it + 4 * wid + g), its 8 k and q values, the
+// v of its rows, alpha and beta.
+template <bool BF16, int NW>
+struct DecItem {
+  static constexpr int kRowsPerStep = 4 * NW;
+  static constexpr int kSteps = kDim / kRowsPerStep;
+  f32x4 s[kSteps][2];  // fp32 rows
+  u32x4 sb[kSteps];    // bf16 rows
+  float k8[8], q8[8], vv[kSteps];
+  float alpha, bt;
+};
+
+// Issues every load of (b, h) with read row rd (-1: zeros): the state first,
+// then the token's inputs.
+template <bool BF16, int NW>
+__device__ __forceinline__ void decode_load(const DecodeParams& p, int b, int h, int64_t rd,
+                                            int wid, int g, int c, DecItem<BF16, NW>& d) {
+  using D = DecItem<BF16, NW>;
+  if (rd >= 0) {
+    if constexpr (BF16) {
+      const u16* src = (const u16*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 8 * c;
+#pragma unroll
+      for (int it = 0; it < D::kSteps; ++it)
+        d.sb[it] = __builtin_nontemporal_load((const u32x4*)(src + (D::kRowsPerStep * it + 4 * wid + g) * kDim));
+    } else {
+      const float* src = (const float*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * c;
+#pragma unroll
+      for (int it = 0; it < D::kSteps; ++it) {
+        const int row = D::kRowsPerStep * it + 4 * wid + g;
+        d.s[it][0] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
+        d.s[it][1] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim + 64));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < D::kSteps; ++it) {
+      d.s[it][0] = d.s[it][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      d.sb[it] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
   const int hq = h / p.group;
-  float k8[8], q8[8];
   if constexpr (BF16) {
     const u16* kp = p.k + ((int64_t)b * p.Hqk + hq) * kDim + 8 * c;
     const u16* qp = p.q + ((int64_t)b * p.Hqk + hq) * kDim + 8 * c;
-    unpack8(*(const u32x4*)kp, k8);
-    unpack8(*(const u32x4*)qp, q8);
+    unpack8(*(const u32x4*)kp, d.k8);
+    unpack8(*(const u32x4*)qp, d.q8);
   } else {
     const u16* kp = p.k + ((int64_t)b * p.Hqk + hq) * kDim + 4 * c;
     const u16* qp = p.q + ((int64_t)b * p.Hqk + hq) * kDim + 4 * c;
     float t[4];
     unpack4(*(const u32x2*)kp, t);
-    for (int i = 0; i < 4; ++i) k8[i] = t[i];
+    for (int i = 0; i < 4; ++i) d.k8[i] = t[i];
     unpack4(*(const u32x2*)(kp + 64), t);
-    for (int i = 0; i < 4; ++i) k8[4 + i] = t[i];
+    for (int i = 0; i < 4; ++i) d.k8[4 + i] = t[i];
     unpack4(*(const u32x2*)qp, t);
-    for (int i = 0; i < 4; ++i) q8[i] = t[i];
+    for (int i = 0; i < 4; ++i) d.q8[i] = t[i];
     unpack4(*(const u32x2*)(qp + 64), t);
-    for (int i = 0; i < 4; ++i) q8[4 + i] = t[i];
+    for (int i = 0; i < 4; ++i) d.q8[4 + i] = t[i];
   }
   const int64_t bh = (int64_t)b * p.H + h;
-  const float alpha = p.g ? expf(p.g[bh]) : 1.f;
-  const float bt = p.beta ? p.beta[bh] : 1.f;
+  d.alpha = p.g ? expf(p.g[bh]) : 1.f;
+  d.bt = p.beta ? p.beta[bh] : 1.f;
+#pragma unroll
+  for (int it = 0; it < D::kSteps; ++it) d.vv[it] = bf2f(p.v[bh * kDim + D::kRowsPerStep * it + 4 * wid + g]);
+}
 
-  // step it covers rows 16*it + 4*wid + g
-  f32x4 s[kSteps][2];  // fp32 rows
-  u32x4 sb[kSteps];    // bf16 rows
-  if (rd >= 0) {
-    if constexpr (BF16) {
-      const u16* src = (const u16*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 8 * c;
-#pragma unroll
-      for (int it = 0; it < kSteps; ++it)
-        sb[it] = __builtin_nontemporal_load((const u32x4*)(src + (kRowsPerStep * it + 4 * wid + g) * kDim));
-    } else {
-      const float* src = (const float*)p.init + rd * p.init_stride + (int64_t)h * kDim * kDim + 4 * c;
-#pragma unroll
-      for (int it = 0; it < kSteps; ++it) {
-        const int row = kRowsPerStep * it + 4 * wid + g;
-        s[it][0] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim));
-        s[it][1] = __builtin_nontemporal_load((const f32x4*)(src + row * kDim + 64));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int it = 0; it < kSteps; ++it) {
-      s[it][0] = s[it][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sb[it] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  float vv[kSteps];
-#pragma unroll
-  for (int it = 0; it < kSteps; ++it) vv[it] = bf2f(p.v[bh * kDim + kRowsPerStep * it + 4 * wid + g]);
-
-  // every product-sum is an explicit fused multiply-add, so the result does
-  // not depend on how the compiler contracts a given instance
+// The update of (b, h) from its loaded values: the new rows to write row wr
+// (-1: no store) and o.  Every product-sum is an explicit fused multiply-add,
+// so the result does not depend on how the compiler contracts an instance.
+template <bool BF16, int NW>
+__device__ __forceinline__ void decode_update(const DecodeParams& p, int b, int h, int64_t wr,
+                                              const DecItem<BF16, NW>& d, int wid, int g, int c) {
+  using D = DecItem<BF16, NW>;
   float kq = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kq = __builtin_fmaf(k8[i], q8[i], kq);
+  for (int i = 0; i < 8; ++i) kq = __builtin_fmaf(d.k8[i], d.q8[i], kq);
   kq = sum16(kq);
-
+  const int64_t bh = (int64_t)b * p.H + h;
   const int64_t doff = wr >= 0 ? wr * p.out_stride + (int64_t)h * kDim * kDim : 0;
   float o_mine = 0.f;  // o of row kRowsPerStep*c + 4*wid + g (lanes c < kSteps)
 #pragma unroll
-  for (int it = 0; it < kSteps; ++it) {
-    const int row = kRowsPerStep * it + 4 * wid + g;
+  for (int it = 0; it < D::kSteps; ++it) {
+    const int row = D::kRowsPerStep * it + 4 * wid + g;
     float sv[8];  // the lane's 8 state values, in k8's order
     if constexpr (BF16) {
-      unpack8(sb[it], sv);
+      unpack8(d.sb[it], sv);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sv[i] = s[it][i >> 2][i & 3];
+      for (int i = 0; i < 8; ++i) sv[i] = d.s[it][i >> 2][i & 3];
     }
     float sk = 0.f, sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sk = __builtin_fmaf(sv[i], k8[i], sk);
-      sq = __builtin_fmaf(sv[i], q8[i], sq);
+      sk = __builtin_fmaf(sv[i], d.k8[i], sk);
+      sq = __builtin_fmaf(sv[i], d.q8[i], sq);
     }
     sk = sum16(sk);
     sq = sum16(sq);
-    const float delta = bt * __builtin_fmaf(-alpha, sk, vv[it]);
+    const float delta = d.bt * __builtin_fmaf(-d.alpha, sk, d.vv[it]);
     float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = __builtin_fmaf(alpha, sv[i], delta * k8[i]);
+    for (int i = 0; i < 8; ++i) y[i] = __builtin_fmaf(d.alpha, sv[i], delta * d.k8[i]);
     if (wr >= 0) {
       if constexpr (BF16) {
         u16* dst = (u16*)p.out + doff + 8 * c;
@@ -184,9 +194,53 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
         __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]}, (f32x4*)(dst + row * kDim + 64));
       }
     }
-    if (c == it) o_mine = p.scale * __builtin_fmaf(alpha, sq, delta * kq);
+    if (c == it) o_mine = p.scale * __builtin_fmaf(d.alpha, sq, delta * kq);
   }
-  if (c < kSteps) p.o[bh * kDim + kRowsPerStep * c + 4 * wid + g] = f2bf(o_mine);
+  if (c < D::kSteps) p.o[bh * kDim + D::kRowsPerStep * c + 4 * wid + g] = f2bf(o_mine);
+}
+
+// One (sequence, v-head) per workgroup.
+template <bool BF16, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+  const int b = blockIdx.x / p.H, h = blockIdx.x - b * p.H;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4;  // row within the wave's 4 rows of a step
+  const int c = lane & 15;  // k = 4c..4c+3 and 64+4c..64+4c+3 (fp32), 8c..8c+7 (bf16)
+  const DecRows r = decode_rows(p, b);
+  DecItem<BF16, NW> d;
+  decode_load(p, b, h, r.rd, wid, g, c, d);
+  decode_update(p, b, h, r.wr, d, wid, g, c);
+}
+
+// A fixed grid walking the (sequence, v-head) pairs blockIdx, blockIdx +
+// gridDim, ...: the next pair's loads (and the rows of the one after) are
+// issued before the current pair is updated, so each workgroup keeps loads
+// in flight instead of waiting on its row indices and state at every start.
+template <bool BF16, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_stream_kernel(const DecodeParams p) {
+  const int items = p.num_seqs * p.H;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  int it = blockIdx.x;
+  if (it >= items) return;
+  DecRows r0 = decode_rows(p, it / p.H);
+  DecItem<BF16, NW> cur;
+  decode_load(p, it / p.H, it % p.H, r0.rd, wid, g, c, cur);
+  int nx = it + (int)gridDim.x;
+  DecRows r1 = nx < items ? decode_rows(p, nx / p.H) : DecRows{-1, -1};
+  for (;;) {
+    DecItem<BF16, NW> nxt;
+    if (nx < items) decode_load(p, nx / p.H, nx % p.H, r1.rd, wid, g, c, nxt);
+    const int nx2 = nx + (int)gridDim.x;
+    const DecRows r2 = nx2 < items ? decode_rows(p, nx2 / p.H) : DecRows{-1, -1};
+    decode_update(p, it / p.H, it % p.H, r0.wr, cur, wid, g, c);
+    if (nx >= items) break;
+    it = nx;
+    nx = nx2;
+    r0 = r1;
+    r1 = r2;
+    cur = nxt;
+  }
 }
 
 }  // namespace
@@ -198,13 +252,41 @@ hipError_t launch_decode_nw(const DecodeParams& p, unsigned blocks, hipStream_t 
   return hipGetLastError();
 }
 
-// Sixteen waves a workgroup (two steps of 64 rows) move the state at 5.6-5.7
-// TB/s on the hybrid step's decode batch, four waves (eight steps) at 5.4-5.5,
-// two and eight waves at 5.2-5.4.  GDN_DECODE_WAVES = 2, 4, 8 or 16 selects
-// one (tests, tuning); the results are bit-identical.
+// Compute units of the current device, queried once per device.
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                   ? n : 256;
+  }
+  return cus[dev];
+}
+
+// fp32 pools: the streaming kernel with 6 workgroups of 16 waves per compute
+// unit, 6.0 TB/s on the hybrid step's decode batch (the one-pair kernel: 5.6;
+// 1-12 per unit: 5.75-6.0); the extra workgroups beyond the resident ones
+// even out the walk's tail.  bf16 pools (half the bytes a pair): the
+// one-pair kernel with 16 waves, 5.5 TB/s (streaming: 4.4-4.6).  One-pair
+// kernels with 4, 2 or 8 waves ran at 5.2-5.5.  GDN_DECODE_STREAM = n (0:
+// off) sets the workgroups per unit, GDN_DECODE_STREAM_GRID the grid itself,
+// GDN_DECODE_WAVES = 2, 4, 8 or 16 a one-pair width (and, alone, selects the
+// one-pair kernel) -- tests, tuning; every choice gives bit-identical results.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0) return hipSuccess;
+  int per_cu = p.state_bf16 || getenv("GDN_DECODE_WAVES") ? 0 : 6;
+  if (const char* f = getenv("GDN_DECODE_STREAM")) per_cu = std::max(0, atoi(f));
+  int64_t grid = (int64_t)device_cus() * per_cu;
+  if (const char* f = getenv("GDN_DECODE_STREAM_GRID")) grid = std::max(0, atoi(f));
+  if (grid > 0) {
+    const unsigned n = (unsigned)std::min<int64_t>(blocks, grid);
+    if (p.state_bf16) decode_stream_kernel<true, 16><<<n, 1024, 0, s>>>(p);
+    else decode_stream_kernel<false, 16><<<n, 1024, 0, s>>>(p);
+    return hipGetLastError();
+  }
   int nw = 16;
   if (const char* f = getenv("GDN_DECODE_WAVES")) nw = atoi(f);
   switch (nw) {
@@ -214,5 +296,4 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
     default: return launch_decode_nw<16>(p, (unsigned)blocks, s);
   }
 }
-
 }  // namespace gdn

@@ -224,15 +224,20 @@ def test_decode_paths_agree_and_match_oracle():
         check_state(pool[r], s)
 
 
-@pytest.mark.parametrize("waves", ["2", "4", "8", "16"])
+@pytest.mark.parametrize("waves", ["2", "4", "8", "16", "stream", "stream-grid-5"])
 def test_decode_every_workgroup_width(waves):
-    """Each decode workgroup shape (2, 4, 8 or 16 waves, 64 / 32 / 16 / 8 rows
-    a wave) against the oracle, fp32 and bf16 pools, GQA and new-page rows."""
+    """Each decode kernel shape against the oracle, fp32 and bf16 pools, GQA
+    and new-page rows: one (sequence, head) per workgroup of 2, 4, 8 or 16
+    waves (64 / 32 / 16 / 8 rows a wave), and the streaming walk -- its
+    default grid, and a grid of 5 workgroups so each walks ~10 pairs through
+    its prefetch pipeline."""
     m = lib()
-    os.environ["GDN_DECODE_WAVES"] = waves
+    env = {"stream": {"GDN_DECODE_STREAM": "6"},
+           "stream-grid-5": {"GDN_DECODE_STREAM_GRID": "5"}}.get(waves, {"GDN_DECODE_WAVES": waves})
+    os.environ.update(env)
     try:
         c = cuda(workloads.config2(num_seqs=12, qk_heads=2, v_heads=4, num_pages=12 * 32,
-                                   new_page_seqs=4, seed=40 + int(waves)))
+                                   new_page_seqs=4, seed=40 + len(waves)))
         dec = c["decode"]
         for pool in (c["pool"], c["pool"].to(torch.bfloat16)):
             rows_in = pool_rows_cpu(pool, dec["read_rows"])
@@ -251,7 +256,8 @@ def test_decode_every_workgroup_width(waves):
             for r, s in writes.items():
                 check_state(pool[r], s)
     finally:
-        del os.environ["GDN_DECODE_WAVES"]
+        for k in env:
+            del os.environ[k]
 
 
 @pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
