@@ -301,7 +301,7 @@ def hybrid(args, torch, gdn, workloads):
     # achieved = algorithmic bytes per call / event-timed call duration.
     traffic = measured_traffic() if L >= 2 else None
     if t_dc_ms >= t_pf_ms:
-        roof = {"kernel": "decode_kernel", "bound": "hbm", "achieved": dc_gbps,
+        roof = {"kernel": "decode_stream_kernel", "bound": "hbm", "achieved": dc_gbps,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dc_gbps / HBM_PEAK_GBPS,
                 "traffic": traffic and traffic["decode"], "per_launch_bytes": dc_bytes,
                 "avg_launch_ms": t_dc_ms}
