@@ -233,7 +233,15 @@ __device__ __forceinline__ void load_tile(u16* tile, const u16* src, int64_t str
   }
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The wait goes through the compiler's own builtin (vmcnt 0, the other
+// counters untouched), so the compiler knows that nothing is outstanding after
+// it: its own waits for stores it issued earlier (whose data registers it must
+// not overwrite before they are read) are then not placed later, where they
+// would also wait for the loads above that it does not know of.
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+  asm volatile("" ::: "memory");
+}
 
 // Scheduling fence for hand-pipelined products: MFMAs and LDS accesses stay
 // on their side (so the next step's operand reads are in flight while this
@@ -697,7 +705,6 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   wait_loads();
   __syncthreads();
 
-  int64_t ckpt_row = -1;  // checkpoint of the previous chunk's end, stored one iteration late
   // the next checkpoint position (the first multiple of the interval past the
   // prefix: the state after the token at that many tokens of the sequence)
   // and its index among the call's checkpoints of this sequence
@@ -730,7 +737,6 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       load_tile<16 / NW>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
       if (outs) load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
-    if (ckpt_row >= 0) store_state_buf(p.ckpt, ckpt_row * p.ckpt_stride + head_off, accS, gq, p.state_bf16);
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
     // Each MFMA run below has vector work beside it that does not depend on
@@ -1022,12 +1028,14 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       }
     }
 
-    // checkpoint at this chunk's end?
-    ckpt_row = -1;
+    // checkpoint at this chunk's end: stored before the wait below, which
+    // then covers the stores too (the state registers are free again before
+    // the next chunk's decay overwrites them)
     if (a_end == ck_next && ck_next <= pre + s.L) {
-      ckpt_row = ld_index(p.ckpt_idx, ck_base + ck_j, p.ckpt_idx64);
+      const int64_t row = ld_index(p.ckpt_idx, ck_base + ck_j, p.ckpt_idx64);
       ++ck_j;
       ck_next += p.ckpt_every;
+      if (row >= 0) store_state_buf(p.ckpt, row * p.ckpt_stride + head_off, accS, gq, p.state_bf16);
     }
     wait_loads();     // the next chunk's tiles have landed (this wave's part)
     __syncthreads();  // ... and every wave's; this chunk's LDS operands are free
@@ -1036,7 +1044,6 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     if constexpr (NW == 8) write_o<2>(p, sm, s, nbase + kChunk * (nch - 1), 2 * wid, lane);
     else write_o_tile<NW>(p, sm, s, nbase + kChunk * (nch - 1), 16 * NW * vt, tid);
   }
-  if (ckpt_row >= 0) store_state_buf(p.ckpt, ckpt_row * p.ckpt_stride + head_off, accS, gq, p.state_bf16);
   if (wr >= 0 && p.out) store_state_buf(p.out, (int64_t)wr * p.out_stride + head_off, accS, gq, p.state_bf16);
   if (wr <= -2) store_state(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, accS, gq);
 }
