@@ -884,18 +884,27 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     // slots 4*(bs&1) + r of P fragment (bt, bs/2).  The ten blocks on and
     // below the diagonal: block w to wave w, and with 8 waves blocks 8 and 9
     // to waves 2 and 3 (which have no loads of the next chunk to issue); the
-    // blocks above it stay at the zeros written before the first chunk.
+    // blocks above it stay at the zeros written before the first chunk.  A
+    // block's eight operand fragments are read before its four products, so
+    // the reads overlap instead of each waiting in turn.
 #pragma unroll
     for (int bi = 0; bi < (NW == 8 ? 2 : (10 + NW - 1) / NW); ++bi) {
       const int blk = NW == 8 ? (bi == 0 ? wid : (wid == 2 || wid == 3 ? wid + 6 : 10)) : wid + NW * bi;
       if (blk >= 10 || !outs) break;
       const int bt = tri_i(blk), bs = tri_j(blk);
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      bf16x8 pk[4], pq[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ks += 2) {
-        acc0 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks, lane), tile_frag(Qb, bt * 4 + ks, lane), acc0);
-        acc1 = mfma16x16x32(tile_frag(Kb, bs * 4 + ks + 1, lane), tile_frag(Qb, bt * 4 + ks + 1, lane), acc1);
+      for (int ks = 0; ks < 4; ++ks) {
+        pk[ks] = tile_frag(Kb, bs * 4 + ks, lane);
+        pq[ks] = tile_frag(Qb, bt * 4 + ks, lane);
       }
+      sched_fence();
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      acc0 = mfma16x16x32(pk[0], pq[0], acc0);
+      acc1 = mfma16x16x32(pk[1], pq[1], acc1);
+      acc0 = mfma16x16x32(pk[2], pq[2], acc0);
+      acc1 = mfma16x16x32(pk[3], pq[3], acc1);
+      sched_fence();
       const f32x4 acc = acc0 + acc1;
       const float Gt = sc[1][16 * bt + n16] + log2_scale;  // P carries the output scale
       const f32x4 Gs = *(const f32x4*)&sc[1][16 * bs + 4 * gq];
@@ -908,13 +917,16 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       const int f = bt * 2 + (bs >> 1);
       *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
     }
-    // K^T fragments wid and wid + 8 (k block mk = f/2, t-step ks = f%2): a K
+    // K^T fragments (k block mk = f/2, t-step ks = f%2; with 8 waves, waves
+    // 0-3 take four each: on each SIMD the older wave w of the pair w, w + 4
+    // wins issue, so waves 4-7 set the pace and get less of this work): a K
     // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
     // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
     // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
 #pragma unroll
-    for (int i = 0; i < 16 / NW; ++i) {
-      const int f = wid + NW * i;
+    for (int i = 0; i < (NW == 8 ? 4 : 16 / NW); ++i) {
+      if (NW == 8 && wid >= 4) break;
+      const int f = NW == 8 ? wid + 4 * i : wid + NW * i;
       const int mk = f >> 1, ks = f & 1;
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
