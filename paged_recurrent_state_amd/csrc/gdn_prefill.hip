@@ -266,8 +266,7 @@ struct WySmem {
   union {
     u16 Kb[kTileWords];      // K tile (row-major, swizzled) ...
     float AT[10][16][kBP];   // ... then A, turning into T block by block
-  } u;
-  float Xs[4][16][17];
+  } u;                       // (X = A[32:64, 0:32] T[0:32, 0:32] goes over the A blocks it consumes)
   float G[kChunk];           // log2-scale running decay sum
   float B[kChunk];           // beta (0 on padding rows)
 };
@@ -424,8 +423,9 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
       bb[j] = use ? tv : 0.f;
     }
     const f32x4 X = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();  // every wave has read its A blocks: X goes over block (I, J)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Xs[wid][4 * gq + r][n16] = X[r];
+    for (int r = 0; r < 4; ++r) sm.u.AT[tri_idx(I, J)][4 * gq + r][n16] = X[r];
   }
   __syncthreads();
   {
@@ -436,11 +436,12 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
       const int kk = perm_row(0, gq, j);  // 0..31 over rows/columns 32..63
       const bool use = I == 3 || kk < 16;  // T_23 = 0
       const float tv = sm.u.AT[tri_idx(I, 2 + (kk >> 4))][n16][kk & 15];
-      const float xv = sm.Xs[(kk >> 4) * 2 + J][kk & 15][n16];
+      const float xv = sm.u.AT[tri_idx(2 + (kk >> 4), J)][kk & 15][n16];  // X
       a[j] = use ? tv : 0.f;
       bb[j] = use ? xv : 0.f;
     }
     const f32x4 Y = mma3(a, bb, f32x4{0.f, 0.f, 0.f, 0.f});
+    __syncthreads();  // every wave has read its X blocks: T goes over block (I, J)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.u.AT[tri_idx(I, J)][4 * gq + r][n16] = -Y[r];
   }
