@@ -200,7 +200,7 @@ def side_measurements(torch, gdn, workloads, pool, dec, ps, H, Hqk, t_dc_ms):
     ws = torch.empty(gdn.prefill_workspace_size(t_max, 1, c["H"], c["Hqk"]), dtype=torch.uint8,
                      device=dev)
 
-    def run():
+    def run(options=None):
         for call in c["calls"]:
             gdn.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
                         call["cu_seqlens"], initial_state=c["pool"],
@@ -210,14 +210,11 @@ def side_measurements(torch, gdn, workloads, pool, dec, ps, H, Hqk, t_dc_ms):
                         checkpoint_state_indices=c["checkpoint_state_indices"],
                         checkpoint_cu_starts=call["checkpoint_cu_starts"],
                         prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=c["every_n"],
-                        workspace=ws)
+                        workspace=ws, options=options)
     T = sum(int(call["q"].shape[0]) for call in c["calls"])
     ms_split = _median_ms(torch, run, 5)
-    os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = "0"
-    try:
-        ms_whole = _median_ms(torch, run, 5)
-    finally:
-        del os.environ["GDN_PREFILL_SPLIT_CHUNKS"]
+    whole = gdn.Options(prefill_split_chunks=-1)
+    ms_whole = _median_ms(torch, lambda: run(whole), 5)
     out["long_prompt"] = {
         "workload": f"one sequence, H=Hqk={c['H']}, {T} tokens in {len(c['calls'])} calls, "
                     f"checkpoints every {c['every_n']}",

@@ -22,8 +22,8 @@
  *                [H, V, K] block and consecutive rows sit `row_stride`
  *                elements apart (>= H*V*K).  The arithmetic is the same for
  *                both types; a bf16 buffer receives each stored state rounded
- *                to nearest even (the page asks for "a state dtype both entry
- *                points support"; fp32 and bf16 both are).
+ *                to nearest even (the page requires one element type that
+ *                both entry points accept; fp32 and bf16 both qualify).
  * Decode uses B (one token per sequence) in place of T.
  * v-head h reads q/k head h / (H / Hqk).
  *
@@ -31,8 +31,10 @@
  * allocate nothing: the caller passes a workspace where one is needed
  * (gdn_prefill_workspace_size).  A call only launches kernels on `stream` (no
  * memset, copy or allocation), so it can be captured into a HIP graph and
- * replayed; the launch decisions (tile width, sequence-parallel split) are
- * taken on the host from the sizes at capture time.  Return value: GDN_OK or a negative status,
+ * replayed; the launch shapes are taken on the host from the sizes and
+ * dims->options, the sequence-parallel plan on the device from the batch's
+ * lengths, so a replay follows the lengths of its own inputs.  Return value:
+ * GDN_OK or a negative status,
  * set before any launch for every check the host can make; the message is in
  * gdn_last_error() (thread-local).  Device-side contents are NOT validated
  * (the page says slots are not checked against the page table): page ids must
@@ -69,7 +71,38 @@ enum {
 enum { GDN_INDEX_INT32 = 0, GDN_INDEX_INT64 = 1 };
 enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 };
 
-/* Head geometry shared by every call. */
+/*
+ * Launch choices of one call.  Every field at 0 selects the library's
+ * default (what the measurements use); the other values exist for tests and
+ * tuning, and every choice computes the same recurrence (decode shapes give
+ * bit-identical results, prefill shapes agree within the tolerances).  The
+ * library reads no environment variables and keeps no per-call settings of
+ * its own: a choice is made by passing it here.  Under HIP graph capture the
+ * choices in force at capture time are frozen into the graph, like any other
+ * argument.
+ *   prefill_split_chunks  sequence-parallel recurrence: 0 = decided on the
+ *                         device from the batch's lengths (possible when
+ *                         B * H <= 256); -1 = never; m > 0 = every sequence in
+ *                         segments of m chunks of 64 tokens.
+ *   prefill_tile_waves    waves per recurrence workgroup: 0 or 8 = whole heads;
+ *                         4, 2 or 1 = V-tiles of 64, 32 or 16 state rows.
+ *   decode_waves          2, 4, 8 or 16: the one-(sequence, head)-per-workgroup
+ *                         decode kernel of that width; 0 = default.
+ *   decode_stream_per_cu  streaming decode workgroups per compute unit;
+ *                         0 = default (6 for fp32 state, one-pair kernel for
+ *                         bf16), -1 = the one-pair kernel.
+ *   decode_stream_grid    > 0: streaming decode with exactly this many
+ *                         workgroups (overrides decode_stream_per_cu).
+ */
+typedef struct {
+  int32_t prefill_split_chunks;
+  int32_t prefill_tile_waves;
+  int32_t decode_waves;
+  int32_t decode_stream_per_cu;
+  int32_t decode_stream_grid;
+} gdn_options_t;
+
+/* Head geometry shared by every call, and the call's launch choices. */
 typedef struct {
   int32_t num_qk_heads; /* Hqk */
   int32_t num_v_heads;  /* H, also the pool's head count */
@@ -77,13 +110,15 @@ typedef struct {
   int32_t head_dim_v;   /* V, must be 128 */
   float scale;          /* output scale; <= 0 selects 1/sqrt(K) */
   int32_t state_dtype;  /* GDN_STATE_F32 or GDN_STATE_BF16: element type of the state buffers */
+  const gdn_options_t* options; /* host pointer, NULL = every default */
 } gdn_dims_t;
 
 /*
  * Per-sequence pool rows of a paged prefill batch, each a device array of
- * [num_seqs] int32 (flashinfer.gdn_paged, GDNPagedPrefillSlots: "all
- * [num_seqs] int32"; the page names state_indices, the other fields are this
- * library's reading of the thin-wrapper description):
+ * [num_seqs] int32 (flashinfer.gdn_paged, GDNPagedPrefillSlots, whose fields
+ * the page gives as one int32 entry per sequence; it names state_indices, the
+ * other fields are this library's reading of the paged call as a wrapper
+ * over the slot arguments):
  *   state_indices         page holding the last prefix token, -1 if no prefix
  *   output_state_indices  last page, -1 for a sequence with no new tokens
  *   checkpoint_cu_starts  indptr[b] + prefix / page_size: where the pages that
@@ -141,14 +176,15 @@ int gdn_decode_slots(const int32_t* page_indices, const int32_t* page_indptr,
  * depends on sizes only and never decreases as either grows, so a workspace
  * sized for the largest call serves every call with at most as many tokens
  * and sequences.  0 on bad dims.
- * Batches whose (sequence, v-head) pairs leave most of the GPU idle (B * H <=
- * 64) and whose sequences are long run the recurrence sequence-parallel:
- * every sequence is cut into segments, each segment's transition S -> S M +
- * N is computed in parallel, the maps are composed in order, and the segments
- * rerun from their true start states.  The workspace then also holds three
- * states (H * V * K floats each) per segment.  The environment variable
- * GDN_PREFILL_SPLIT_CHUNKS = m, read at every call (also by this function),
- * forces segments of m chunks of 64 tokens; 0 turns the split off.
+ * Batches whose (sequence, v-head) pairs fill at most the chip's compute
+ * units once (B * H <= 256) may run the recurrence sequence-parallel: a long
+ * sequence is cut into segments, each segment's transition S -> S M + N is
+ * computed in parallel, the maps are composed in order, and the segments
+ * rerun from their true start states.  Whether and how finely to cut is
+ * decided on the device from the batch's actual lengths (or forced through
+ * dims->options); the workspace then also holds three states (H * V * K
+ * floats each) per segment, for at most 512 / H + B segments.  The size
+ * depends on dims->options (prefill_split_chunks) as the call does.
  */
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs,
                                   const gdn_dims_t* dims);

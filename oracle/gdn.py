@@ -13,25 +13,30 @@ The output uses the state AFTER the token's update.  ``g`` absent means
 them optional).  With fewer q/k heads than v-heads, v-head ``h`` uses q/k head
 ``h // (H / Hqk)``.
 
-Row semantics (flashinfer.gdn_paged, "Slot arguments of chunk_gated_delta_rule"):
+Row semantics, restated from flashinfer.gdn_paged, section "Slot arguments of
+chunk_gated_delta_rule":
 
-* a read row of -1 starts from the zero state (literal zeros, never a loaded
-  row times 0, which would keep a NaN alive);
-* a write row of -1 skips the final-state store, and a zero-length sequence
-  writes nothing;
-* checkpoint ``j`` of sequence ``i`` goes to row
-  ``checkpoint_state_indices[checkpoint_cu_starts[i] + j]`` (skipped when -1),
-  taken after new token ``n`` whenever ``(prefix_lens[i] + n)`` is a multiple
-  of ``checkpoint_every_n_tokens``;
-* initial state, output state and checkpoints may be one pool; rows written by
-  one sequence may be neither read nor written by another sequence of the call.
+* the zero state is used where the read row is -1 (built from literal zeros:
+  multiplying a loaded row by 0 would keep a NaN in it);
+* where the write row is -1 the final state is not stored; a sequence with no
+  new tokens stores nothing at all;
+* a sequence's checkpoints are numbered from 0 in the order they occur; the
+  j-th of sequence ``i`` is stored in row
+  ``checkpoint_state_indices[checkpoint_cu_starts[i] + j]`` (nothing is stored
+  where that entry is -1), and one occurs after new token ``n`` whenever
+  ``prefix_lens[i] + n`` is divisible by ``checkpoint_every_n_tokens``;
+* the three state buffers may alias one pool, and a row that a sequence
+  writes must not be touched (read or written) by any other sequence of the
+  same call.
 
 No chunking, no padding, no blocking: one token at a time, all heads of the
 token at once in fp64.  Inputs are upcast exactly (bf16 and fp32 values are
 representable in fp64).
 
-State dtype.  The first page asks only that a pool used by both entry points
-hold "a state dtype both support".  Reading: every state buffer of a call has
+State dtype.  The first page requires only that a pool shared by the prefill
+and the decode entry points use an element type that both accept (pool
+paragraph of flashinfer.gdn_paged, "Page table").  Reading: every state buffer
+of a call has
 one element type, fp32 or bf16; the arithmetic is unchanged, and a state is
 rounded to the buffer's type only where it is stored (checkpoints and the
 final state), to nearest with ties to even.  ``state_dtype="bf16"`` applies

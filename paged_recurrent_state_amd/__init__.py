@@ -8,6 +8,7 @@ Build the library with ``python -m paged_recurrent_state_amd.build``.
 from ._lib import (  # noqa: F401
     DecodeSlots,
     GDNError,
+    Options,
     PrefillSlots,
     block_table_to_csr,
     csr_to_block_table,

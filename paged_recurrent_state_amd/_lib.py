@@ -28,10 +28,23 @@ class GDNError(RuntimeError):
         self.code = code
 
 
+class Options(C.Structure):
+    """Launch choices of one call (gdn_options_t); every field 0 = the default.
+
+    prefill_split_chunks: 0 the device decides from the lengths, -1 never
+    split, m > 0 segments of m chunks.  prefill_tile_waves: 0/8 whole heads,
+    4/2/1 V-tiles.  decode_waves: 2/4/8/16 one-pair decode width.
+    decode_stream_per_cu: streaming decode workgroups per CU (-1 off).
+    decode_stream_grid: streaming decode grid."""
+    _fields_ = [("prefill_split_chunks", C.c_int32), ("prefill_tile_waves", C.c_int32),
+                ("decode_waves", C.c_int32), ("decode_stream_per_cu", C.c_int32),
+                ("decode_stream_grid", C.c_int32)]
+
+
 class Dims(C.Structure):
     _fields_ = [("num_qk_heads", C.c_int32), ("num_v_heads", C.c_int32),
                 ("head_dim_k", C.c_int32), ("head_dim_v", C.c_int32), ("scale", C.c_float),
-                ("state_dtype", C.c_int32)]
+                ("state_dtype", C.c_int32), ("options", C.POINTER(Options))]
 
 
 # element types of the state buffers (gdn_dims_t.state_dtype)
@@ -172,10 +185,14 @@ def _pool_stride(pool: torch.Tensor, name: str, H: int, V: int, K: int) -> int:
     return pool.stride(0) if pool.shape[0] > 1 else H * V * K
 
 
-def _dims(q, v, scale, state_dtype: int = 0):
+def _dims(q, v, scale, state_dtype: int = 0, options: Optional[Options] = None):
     Hqk, K = q.shape[-2], q.shape[-1]
     H, V = v.shape[-2], v.shape[-1]
-    return Dims(Hqk, H, K, V, float(scale) if scale else 0.0, state_dtype)
+    if options is not None and not isinstance(options, Options):
+        raise TypeError("options must be a paged_recurrent_state_amd.Options")
+    # the structure keeps `options` referenced for as long as it lives
+    return Dims(Hqk, H, K, V, float(scale) if scale else 0.0, state_dtype,
+                C.pointer(options) if options is not None else None)
 
 
 def _token_checks(q, k, v, g, beta, dev, T):
@@ -194,8 +211,10 @@ def _token_checks(q, k, v, g, beta, dev, T):
 
 
 def prefill_workspace_size(total_tokens: int, num_seqs: int, num_v_heads: int,
-                           num_qk_heads: int, head_dim: int = 128) -> int:
-    d = Dims(num_qk_heads, num_v_heads, head_dim, head_dim, 0.0)
+                           num_qk_heads: int, head_dim: int = 128,
+                           options: Optional[Options] = None) -> int:
+    d = Dims(num_qk_heads, num_v_heads, head_dim, head_dim, 0.0, 0,
+             C.pointer(options) if options is not None else None)
     return int(load().gdn_prefill_workspace_size(int(total_tokens), int(num_seqs), C.byref(d)))
 
 
@@ -303,7 +322,8 @@ def csr_to_block_table(page_indptr, page_indices, last_page_len, page_size: int,
 def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_indptr,
                   page_size: int, last_page_len, slots: Optional[PrefillSlots] = None,
                   scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None,
+                  options: Optional[Options] = None) -> torch.Tensor:
     """Chunked GDN prefill reading and writing a paged state pool; returns o [T, H, V] bf16."""
     lib = load()
     dev = q.device
@@ -312,7 +332,7 @@ def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_i
     for t, nm in ((cu_seqlens, "cu_seqlens"), (page_indices, "page_indices"),
                   (page_indptr, "page_indptr"), (last_page_len, "last_page_len")):
         _need(t, nm, torch.int32, dev)
-    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")))
+    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")), options)
     stride = _pool_stride(state_pool, "state_pool", d.num_v_heads, d.head_dim_v, d.head_dim_k)
     B = last_page_len.shape[0]
     o = out if out is not None else torch.empty(T, d.num_v_heads, d.head_dim_v,
@@ -333,7 +353,8 @@ def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_i
 
 def decode_paged(q, k, v, g, beta, state_pool, page_indices, page_indptr, page_size: int,
                  last_page_len, slots: Optional[DecodeSlots] = None,
-                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                 options: Optional[Options] = None) -> torch.Tensor:
     """Single-token GDN decode on a paged pool; returns o [B, H, V] bf16."""
     lib = load()
     dev = q.device
@@ -342,7 +363,7 @@ def decode_paged(q, k, v, g, beta, state_pool, page_indices, page_indptr, page_s
     for t, nm in ((page_indices, "page_indices"), (page_indptr, "page_indptr"),
                   (last_page_len, "last_page_len")):
         _need(t, nm, torch.int32, dev)
-    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")))
+    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")), options)
     stride = _pool_stride(state_pool, "state_pool", d.num_v_heads, d.head_dim_v, d.head_dim_k)
     o = out if out is not None else torch.empty(B, d.num_v_heads, d.head_dim_v,
                                                 dtype=torch.bfloat16, device=dev)
@@ -363,7 +384,8 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=N
             state_checkpoints=None, checkpoint_state_indices=None, checkpoint_cu_starts=None,
             prefix_lens=None, checkpoint_every_n_tokens: int = 0,
             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None,
+            options: Optional[Options] = None) -> torch.Tensor:
     """Slot-argument chunked prefill (the general form the paged call wraps)."""
     lib = load()
     dev = q.device
@@ -379,7 +401,7 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=N
             _need(t, nm, t.dtype, dev)
     bufs = ((initial_state, "initial_state"), (output_state, "output_state"),
             (state_checkpoints, "state_checkpoints"))
-    d = _dims(q, v, scale, _state_dtype(dev, *bufs))
+    d = _dims(q, v, scale, _state_dtype(dev, *bufs), options)
     H, V, K = d.num_v_heads, d.head_dim_v, d.head_dim_k
     strides = []
     for t, nm in bufs:
@@ -403,7 +425,8 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, initial_state=None, state_indices=N
 
 def decode(q, k, v, g, beta, *, initial_state=None, initial_state_indices=None,
            output_state=None, output_state_indices=None, scale: Optional[float] = None,
-           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+           out: Optional[torch.Tensor] = None,
+           options: Optional[Options] = None) -> torch.Tensor:
     """Single-token step with explicit rows; returns o [B, H, V] bf16."""
     lib = load()
     dev = q.device
@@ -415,7 +438,7 @@ def decode(q, k, v, g, beta, *, initial_state=None, initial_state_indices=None,
         if t is not None:
             _need(t, nm, t.dtype, dev)
     d = _dims(q, v, scale, _state_dtype(dev, (initial_state, "initial_state"),
-                                        (output_state, "output_state")))
+                                        (output_state, "output_state")), options)
     H, V, K = d.num_v_heads, d.head_dim_v, d.head_dim_k
     s_in = s_out = 0
     if initial_state is not None:

@@ -5,7 +5,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -46,64 +45,75 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // fragments + scalars).
 // A sequence with L new tokens spans ceil(((prefix mod 64) + L) / 64) <=
 // (L + 126) / 64 chunks, so a batch never has more than T / 64 + 2 B of them.
-// With the sequence-parallel recurrence (split_m > 0) it also holds the
-// segment records of both passes, the per-sequence scan records and the
-// segment states (start, offset and transition of every segment: at most 3
-// per segment, rows of H * V * K floats).
+// With the sequence-parallel recurrence it also holds the segment records of
+// both passes, the per-sequence scan records and the segment states (a
+// sequence of G >= 2 segments keeps 3 G - 2 states: its G start states and
+// the offset and transition of every segment but the last; rows of H * V * K
+// floats), room for `segs` segments.
 struct WsLayout {
   int64_t nc;
-  int split_m;
+  int split_mode, split_m;
   int64_t cap1, cap2, rows;
   size_t slots, order, zero, tab, T, scal, seg1, seg2, scan, counts, states, total;
 };
 
-// Segment length (chunks) of the sequence-parallel recurrence, 0 for whole
-// sequences.  With n = B * H (sequence, v-head) pairs on the chip's 256
-// compute units, whole sequences take one round of c chunks; G segments per
-// sequence take about two rounds of c / G chunks for the first pass (2G - 2
-// runs per sequence, without outputs) and one for the second (G runs), plus
-// G - 1 scan steps.  G = 256 / n fills the second pass once, and the split
-// wins by about G / 3: only when n <= 64 and the sequences are long.
-// GDN_PREFILL_SPLIT_CHUNKS = m forces segments of m chunks (0: never split).
-// GDN_PREFILL_SPLIT_CHUNKS as set (m >= 0), or -1 when it is not
-int forced_split() {
-  const char* f = getenv("GDN_PREFILL_SPLIT_CHUNKS");
-  return f ? std::max(0, atoi(f)) : -1;
+// Launch choices of a call, from dims->options (NULL: all defaults).
+struct Opts {
+  int split;   // gdn_options_t.prefill_split_chunks
+  int waves;   // recurrence workgroup width
+  DecodeShape dec;
+};
+
+Opts get_opts(const gdn_dims_t* d) {
+  Opts o{0, 8, DecodeShape{0, 0, 0}};
+  if (d && d->options) {
+    const gdn_options_t* x = d->options;
+    o.split = x->prefill_split_chunks;
+    o.waves = x->prefill_tile_waves ? x->prefill_tile_waves : 8;
+    o.dec = DecodeShape{x->decode_waves, x->decode_stream_per_cu, x->decode_stream_grid};
+  }
+  return o;
 }
 
-int split_chunks(int64_t T, int B, int H) {
-  if (const int m = forced_split(); m >= 0) return m;
-  const int64_t n = (int64_t)B * H;
-  if (B <= 0 || n > 64) return 0;
-  const int64_t nc = T / kChunk + 2 * (int64_t)B;
-  if (nc < 16 * (int64_t)B) return 0;  // short sequences: nothing to win
-  const int64_t G = 256 / n;              // segments per sequence
-  return (int)std::max<int64_t>(4, (nc + B * G - 1) / (B * G));
+// The auto plan is possible when the batch's (sequence, head) pairs fill the
+// compute units at most once and there are enough tokens for a sequence of
+// 16 chunks; its segments are bounded by kSplitMaxPerHead / H + B (beyond
+// that, the second pass alone would take several rounds of the chip) and by
+// chunks / kSplitMinChunks + B.
+constexpr int64_t kAutoMinTokens = 16 * kChunk;
+bool auto_allowed(int64_t T, int64_t B, int H) {
+  return B >= 1 && B * H <= 256 && T >= kAutoMinTokens;
+}
+int64_t auto_segments(int64_t T, int64_t B, int H) {
+  const int64_t nc = T / kChunk + 2 * B + 1;
+  return std::min<int64_t>(nc / kSplitMinChunks + B, kSplitMaxPerHead / H + B);
 }
 
 // Workspace regions for a call of T tokens in B sequences.  With `bound`,
 // the sequence-parallel regions are sized for every call of at most T tokens
 // and B sequences (the size query: one workspace serves every smaller call);
-// without, for this call's own segments (the layout a call uses).
-WsLayout ws_layout(int64_t T, int B, int H, bool bound = false) {
+// without, for this call's own plan (the layout a call uses).
+WsLayout ws_layout(int64_t T, int B, int H, int split_opt, bool bound = false) {
   WsLayout w;
   w.nc = T / kChunk + 2 * (int64_t)B + 1;
-  w.split_m = split_chunks(T, B, H);
-  // a sequence of c chunks has ceil(c / m) <= c / m + 1 segments
-  int64_t segs = w.split_m > 0 ? w.nc / w.split_m + B : 0;
-  if (bound && forced_split() < 0 && H <= 64) {
-    // A call of T' <= T tokens in B' <= B sequences splits only when B' H <=
-    // 64 and T' / 64 >= 14 B'.  Its m is at least 4 and at least nc' / (B' G')
-    // with G' = 256 / (B' H), so it has at most (nc' + 1) / m + B' segments:
-    // <= B' G' (1 + 1/16) + B' and <= (T / 64 + 2 B' + 1) / 4 + B'.  Both
-    // bounds grow with T and B, so the size does too.
-    const int64_t bmax = std::min<int64_t>({(int64_t)B, 64 / H, T / (14 * kChunk)});
-    if (bmax >= 1) {
-      const int64_t G1 = 256 / H;
-      const int64_t by_g = G1 + G1 / 16 + 1 + bmax;
-      const int64_t by_t = (T / kChunk + 2 * bmax + 1) / 4 + bmax;
-      segs = std::max(segs, std::min(by_g, by_t));
-    }
+  int64_t segs = 0;
+  w.split_m = 0;
+  if (split_opt > 0) {  // forced: a sequence of c chunks has ceil(c / m) <= c / m + 1 segments
+    w.split_mode = kSplitForced;
+    w.split_m = split_opt;
+    segs = w.nc / split_opt + B;
+  } else if (split_opt == 0 && auto_allowed(T, B, H)) {
+    w.split_mode = kSplitAuto;
+    segs = auto_segments(T, B, H);
+  } else {
+    w.split_mode = kSplitOff;
+  }
+  if (bound && split_opt == 0) {
+    // every call of T' <= T tokens in B' <= B sequences that takes the auto
+    // plan has B' <= min(B, 256 / H) and T' >= 16 chunks; its room grows with
+    // T' and B', so the largest such call bounds them all
+    const int64_t bmax = std::min<int64_t>(B, 256 / H);
+    if (bmax >= 1 && T >= kAutoMinTokens) segs = std::max(segs, auto_segments(T, bmax, H));
   }
   w.cap1 = 2 * segs;
   w.cap2 = segs;
@@ -138,6 +148,23 @@ WsLayout ws_layout(int64_t T, int B, int H, bool bound = false) {
   return w;
 }
 
+int check_opts(const gdn_dims_t* d) {
+  if (!d->options) return GDN_OK;
+  const gdn_options_t* x = d->options;
+  if (x->prefill_split_chunks < -1)
+    return fail(GDN_EINVAL, "options.prefill_split_chunks must be -1, 0 or positive (got %d)",
+                x->prefill_split_chunks);
+  const int w = x->prefill_tile_waves;
+  if (w != 0 && w != 1 && w != 2 && w != 4 && w != 8)
+    return fail(GDN_EINVAL, "options.prefill_tile_waves must be 0, 1, 2, 4 or 8 (got %d)", w);
+  const int dw = x->decode_waves;
+  if (dw != 0 && dw != 2 && dw != 4 && dw != 8 && dw != 16)
+    return fail(GDN_EINVAL, "options.decode_waves must be 0, 2, 4, 8 or 16 (got %d)", dw);
+  if (x->decode_stream_per_cu < -1 || x->decode_stream_grid < 0)
+    return fail(GDN_EINVAL, "options.decode_stream_per_cu must be >= -1 and decode_stream_grid >= 0");
+  return GDN_OK;
+}
+
 int check_dims(const gdn_dims_t* d) {
   if (!d) return fail(GDN_EINVAL, "dims is NULL");
   if (d->num_qk_heads <= 0 || d->num_v_heads <= 0)
@@ -152,7 +179,7 @@ int check_dims(const gdn_dims_t* d) {
   if (d->state_dtype != GDN_STATE_F32 && d->state_dtype != GDN_STATE_BF16)
     return fail(GDN_EINVAL, "state_dtype must be GDN_STATE_F32 or GDN_STATE_BF16 (got %d)",
                 d->state_dtype);
-  return GDN_OK;
+  return check_opts(d);
 }
 
 float eff_scale(const gdn_dims_t* d) {
@@ -216,7 +243,10 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.ckpt_idx = ckpt_idx;
   pp.ckpt_idx64 = ckpt_idx64;
   pp.ckpt_every = ckpt_every;
+  pp.split_mode = L.split_mode;
   pp.split_m = L.split_m;
+  pp.num_cus = device_cus();
+  pp.tile_waves = get_opts(d).waves;
   pp.seg_cap1 = (int)L.cap1;
   pp.seg_cap2 = (int)L.cap2;
   pp.seg1 = (int32_t*)((char*)ws + L.seg1);
@@ -233,15 +263,36 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
 
 }  // namespace
 
+namespace gdn {
+
+int current_device() {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
+int device_cus() {
+  static int cus[kMaxDevices] = {0};
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                   ? n : 256;
+  }
+  return cus[dev];
+}
+
+}  // namespace gdn
+
 extern "C" {
 
 const char* gdn_last_error(void) { return g_err.c_str(); }
 
-const char* gdn_version(void) { return "gdn_paged 0.1.0 (gfx950)"; }
+const char* gdn_version(void) { return "gdn_paged 0.2.0 (gfx950)"; }
 
 size_t gdn_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, const gdn_dims_t* dims) {
   if (check_dims(dims) != GDN_OK || total_tokens < 0 || num_seqs < 0) return 0;
-  return ws_layout(total_tokens, num_seqs, dims->num_v_heads, true).total;
+  return ws_layout(total_tokens, num_seqs, dims->num_v_heads, get_opts(dims).split, true).total;
 }
 
 int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,
@@ -339,7 +390,7 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
   if (num_seqs == 0) return ok();
   if (total_tokens > 0)
     if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads);
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, get_opts(dims).split);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
@@ -414,7 +465,7 @@ int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const
     dp.page_indptr = page_indptr;
     dp.last_page_len = last_page_len;
   }
-  if (int rc = launched(launch_decode(dp, stream), "decode kernel")) return rc;
+  if (int rc = launched(launch_decode(dp, get_opts(dims).dec, stream), "decode kernel")) return rc;
   return ok();
 }
 
@@ -453,7 +504,7 @@ int gdn_prefill(const gdn_dims_t* dims, const void* q, const void* k, const void
   }
   if (num_seqs == 0 || total_tokens == 0) return ok();
   if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads);
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, get_opts(dims).split);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
@@ -513,7 +564,7 @@ int gdn_decode(const gdn_dims_t* dims, const void* q, const void* k, const void*
   dp.init_stride = initial_row_stride;
   dp.out = output_state;
   dp.out_stride = output_row_stride;
-  if (int rc = launched(launch_decode(dp, stream), "decode kernel")) return rc;
+  if (int rc = launched(launch_decode(dp, get_opts(dims).dec, stream), "decode kernel")) return rc;
   return ok();
 }
 

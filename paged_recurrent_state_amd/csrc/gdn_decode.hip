@@ -24,7 +24,6 @@
 // Loads and stores bypass the caches' retention (non-temporal): every byte is
 // touched once.
 #include <algorithm>
-#include <cstdlib>
 
 #include "gdn_internal.h"
 
@@ -252,44 +251,29 @@ hipError_t launch_decode_nw(const DecodeParams& p, unsigned blocks, hipStream_t 
   return hipGetLastError();
 }
 
-// Compute units of the current device, queried once per device.
-static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int n = 0;
-    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
-                   ? n : 256;
-  }
-  return cus[dev];
-}
-
 // fp32 pools: the streaming kernel with 6 workgroups of 16 waves per compute
 // unit, 6.0 TB/s on the hybrid step's decode batch (the one-pair kernel: 5.6;
 // 1-12 per unit: 5.75-6.0); the extra workgroups beyond the resident ones
 // even out the walk's tail.  bf16 pools (half the bytes a pair): the
 // one-pair kernel with 16 waves, 5.5 TB/s (streaming: 4.4-4.6).  One-pair
-// kernels with 4, 2 or 8 waves ran at 5.2-5.5.  GDN_DECODE_STREAM = n (0:
-// off) sets the workgroups per unit, GDN_DECODE_STREAM_GRID the grid itself,
-// GDN_DECODE_WAVES = 2, 4, 8 or 16 a one-pair width (and, alone, selects the
-// one-pair kernel) -- tests, tuning; every choice gives bit-identical results.
-hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
+// kernels with 4, 2 or 8 waves ran at 5.2-5.5.  The shape arguments pick
+// another (tests, tuning); every choice gives bit-identical results.
+hipError_t launch_decode(const DecodeParams& p, const DecodeShape& shape, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0) return hipSuccess;
-  int per_cu = p.state_bf16 || getenv("GDN_DECODE_WAVES") ? 0 : 6;
-  if (const char* f = getenv("GDN_DECODE_STREAM")) per_cu = std::max(0, atoi(f));
+  // a one-pair width asked for alone selects the one-pair kernel
+  int per_cu = p.state_bf16 || shape.waves ? 0 : 6;
+  if (shape.stream_per_cu > 0) per_cu = shape.stream_per_cu;
+  if (shape.stream_per_cu < 0) per_cu = 0;
   int64_t grid = (int64_t)device_cus() * per_cu;
-  if (const char* f = getenv("GDN_DECODE_STREAM_GRID")) grid = std::max(0, atoi(f));
+  if (shape.stream_grid > 0) grid = shape.stream_grid;
   if (grid > 0) {
     const unsigned n = (unsigned)std::min<int64_t>(blocks, grid);
     if (p.state_bf16) decode_stream_kernel<true, 16><<<n, 1024, 0, s>>>(p);
     else decode_stream_kernel<false, 16><<<n, 1024, 0, s>>>(p);
     return hipGetLastError();
   }
-  int nw = 16;
-  if (const char* f = getenv("GDN_DECODE_WAVES")) nw = atoi(f);
-  switch (nw) {
+  switch (shape.waves) {
     case 2: return launch_decode_nw<2>(p, (unsigned)blocks, s);
     case 4: return launch_decode_nw<4>(p, (unsigned)blocks, s);
     case 8: return launch_decode_nw<8>(p, (unsigned)blocks, s);

@@ -40,6 +40,14 @@ constexpr int kRecScal = 4 * kChunk;           // floats (1 KiB)
 // first chunk slot, read row, write row, first checkpoint index, mode}.
 // Rows: >= 0 a row of the caller's state buffers, -1 none (zero state / no
 // store), <= -2 row (-2 - r) of the workspace's segment states.
+// split_mode: off (whole sequences, one recurrence launch), forced (segments
+// of split_m chunks) or auto (the plan kernel picks m, or no split, from the
+// batch's chunk counts).
+constexpr int kSplitOff = 0;
+constexpr int kSplitForced = 1;
+constexpr int kSplitAuto = 2;
+constexpr int kSplitMinChunks = 4;  // shortest segment the auto plan considers
+constexpr int kSplitMaxPerHead = 512;  // auto plan: segments <= kSplitMaxPerHead / H + B
 constexpr int kSegWords = 8;
 constexpr int kSegNormal = 0;  // a real run: outputs, checkpoints, final state
 constexpr int kSegOffset = 1;  // from the zero state, no outputs: the segment's offset N
@@ -76,8 +84,11 @@ struct PrefillParams {
   const void* ckpt_idx;
   int ckpt_idx64;
   int ckpt_every;
-  // sequence-parallel recurrence (split_m > 0: segments of split_m chunks)
-  int split_m;
+  // sequence-parallel recurrence
+  int split_mode;          // kSplitOff / kSplitForced / kSplitAuto
+  int split_m;             // forced segment length (chunks)
+  int num_cus;             // compute units of the device (auto plan's cost model)
+  int tile_waves;          // waves per recurrence workgroup (8: whole heads)
   int seg_cap1, seg_cap2;  // segment records the two passes have room for
   int32_t* seg1;           // [seg_cap1][kSegWords] first pass (workspace)
   int32_t* seg2;           // [seg_cap2][kSegWords] second pass (workspace)
@@ -138,7 +149,19 @@ hipError_t launch_csr_to_block_table(const int32_t* indptr, const int32_t* indic
                                      int32_t* table, int64_t row_stride, int32_t* ctx,
                                      int32_t* bad, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s);
-hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+// Decode launch shape (all 0: the default; see gdn_options_t).
+struct DecodeShape {
+  int waves;       // one-pair kernel width (2, 4, 8, 16), 0 = default
+  int stream_per_cu;  // streaming workgroups per compute unit, 0 = default, -1 = off
+  int stream_grid;    // streaming grid, 0 = from stream_per_cu
+};
+hipError_t launch_decode(const DecodeParams& p, const DecodeShape& shape, hipStream_t s);
+
+// Compute units of the current device (queried once per device).
+int device_cus();
+// Index of the current device, or -1 (for per-device caches of size kMaxDevices).
+constexpr int kMaxDevices = 64;
+int current_device();
 
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)

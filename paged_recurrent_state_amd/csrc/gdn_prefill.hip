@@ -36,8 +36,6 @@
 //   2 when one side is exact bf16), which keeps ~2^-17 relative accuracy.
 //   The next chunk's tiles load straight from global memory into
 //   double-buffered LDS while the current one computes.
-#include <cstdlib>
-
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -1130,18 +1128,115 @@ __device__ void plan_body(const int32_t* __restrict__ cu, const int32_t* __restr
 
 // Sequence-parallel plan, one workgroup.  Sequence b (G = ceil(chunks / m)
 // segments of m chunks; segment g starts at new token lo_g, an absolute
-// multiple of 64 for g >= 1) gets:
+// multiple of 64 for g >= 1) gets, when G >= 2:
 //   first pass:  for g = 0 .. G-2 the segment from the zero state (its offset
 //                N_g) and from the identity with v = 0 (its transition M_g),
 //                so that S_end = S_start M_g + N_g;
-//   scan:        start_0 = the sequence's initial state, start_{g+1} =
-//                start_g M_g + N_g, g = 0 .. G-2;
-//   second pass: segments 0 .. G-1 for real from start_g (start_0: the read
-//                row), the last one writing the final state.
-// Workspace state rows of b, from row0: start_1 .. start_{G-1}, then
-// N_0 .. N_{G-2}, then M_0 .. M_{G-2}.
+//   scan:        start_0 = the sequence's initial state, copied into the
+//                workspace; start_{g+1} = start_g M_g + N_g, g = 0 .. G-2;
+//   second pass: segments 0 .. G-1 for real from start_g, the last one
+//                writing the final state.
+// Workspace state rows of b, from row0: start_0 .. start_{G-1}, then
+// N_0 .. N_{G-2}, then M_0 .. M_{G-2} (3G - 2 rows).  No launch both reads and
+// writes a caller row: the first pass reads none, the scan reads the
+// initial state and writes only workspace rows, and the second pass reads
+// only workspace rows (segment 0 too) while it stores checkpoints and final
+// states -- so an in-place update (write row = read row) or a prefix page
+// that a later segment checkpoints never depends on the order in which the
+// second pass's workgroups run.  A sequence with G = 1 runs whole in the
+// second pass from its own read row, in one workgroup per (sequence, head,
+// V-tile) that reads before it writes.
+
+// Auto plan: the cost, in chunks of the whole-sequence recurrence on one
+// compute unit, of running the batch whole and cut into segments of m
+// chunks, and the m (or none) that costs least.  Items are (sequence, head)
+// runs, P of them resident at once (one recurrence workgroup per compute
+// unit); a pass of items of at most m chunks takes about m per round of P.
+//   whole:  max(c_max, H sum(c) / P)
+//   split:  first pass  a1 m ceil(2 H sum(G - 1) / P)
+//           scan        a_s (G_max - 1) ceil(8 B H / CUs)   (8 workgroups a pair)
+//           second pass max(m, H sum(c) / P)
+//           + launches  a_l
+// with a1 the relative cost of a first-pass chunk (no outputs) and a_s of
+// one composition step of the scan.
+constexpr float kCostPass1 = 0.8f;
+constexpr float kCostScanStep = 0.5f;
+constexpr float kCostLaunches = 2.0f;
+constexpr int kAutoMaxSegs = 65;  // candidates: the longest sequence in 2 .. 65 segments
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+// Segment length of the auto plan (0: whole sequences), the same in every
+// thread.  B <= 256 (the host enables the auto plan only when B H <= 256).
+__device__ int auto_split_m(const PrefillParams& p) {
+  __shared__ int cnt[256];
+  if (p.num_seqs > 256) return 0;
+  __shared__ float wcost[kPlanTile / 64];
+  __shared__ int wm[kPlanTile / 64];
+  const int B = p.num_seqs, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  if (tid < B) cnt[tid] = chunks_of(p.slots.prefix[tid], p.cu_seqlens[tid + 1] - p.cu_seqlens[tid]);
+  __syncthreads();
+  int cmax = 0, csum = 0;
+  for (int i = lane; i < B; i += 64) {
+    cmax = max(cmax, cnt[i]);
+    csum += cnt[i];
+  }
+  cmax = wave_max(cmax);
+  csum = wave_sum(csum);
+  const float P = fmaxf(1.f, (float)(p.num_cus * p.tile_waves / 8));
+  const float H = (float)p.H;
+  const float rounds_scan = ceilf(8.f * B * p.H / fmaxf(1.f, (float)p.num_cus));
+  float best = fmaxf((float)cmax, H * csum / P);
+  int best_m = 0;
+  for (int G = 2 + wid; G <= kAutoMaxSegs; G += nw) {
+    const int m = max(kSplitMinChunks, (cmax + G - 1) / G);
+    if (m >= cmax) continue;  // nothing would be cut
+    int sg = 0, sg1 = 0, gmax = 0;
+    for (int i = lane; i < B; i += 64) {
+      const int g = (cnt[i] + m - 1) / m;
+      sg += g;
+      sg1 += max(g - 1, 0);
+      gmax = max(gmax, g);
+    }
+    sg = wave_sum(sg);
+    sg1 = wave_sum(sg1);
+    gmax = wave_max(gmax);
+    if (sg > p.seg_cap2 || 2 * sg1 > p.seg_cap1) continue;  // beyond the workspace's room
+    const float cost = kCostPass1 * m * ceilf(2.f * H * sg1 / P) + kCostScanStep * (gmax - 1) * rounds_scan +
+                       fmaxf((float)m, H * csum / P) + kCostLaunches;
+    if (cost < best) {
+      best = cost;
+      best_m = m;
+    }
+  }
+  if (lane == 0) {
+    wcost[wid] = best;
+    wm[wid] = best_m;
+  }
+  __syncthreads();
+  float b = wcost[0];
+  int bm = wm[0];
+  for (int w = 1; w < nw; ++w)
+    if (wcost[w] < b || (wcost[w] == b && wm[w] > bm)) {
+      b = wcost[w];
+      bm = wm[w];
+    }
+  return bm;
+}
+
 __device__ void split_plan(const PrefillParams& p) {
-  const int m = p.split_m, B = p.num_seqs;
+  const int m = p.split_mode == kSplitAuto ? auto_split_m(p) : p.split_m;
+  const int B = p.num_seqs;
   int carry1 = 0, carry2 = 0, carry_row = 0;
   for (int base = 0; base < B; base += blockDim.x) {
     const int b = base + (int)threadIdx.x;
@@ -1149,9 +1244,10 @@ __device__ void split_plan(const PrefillParams& p) {
     if (b < B) {
       L = p.cu_seqlens[b + 1] - p.cu_seqlens[b];
       pre = p.slots.prefix[b];
-      G = L > 0 ? (chunks_of(pre, L) + m - 1) / m : 0;
+      const int c = chunks_of(pre, L);
+      G = L <= 0 ? 0 : m > 0 ? (c + m - 1) / m : 1;
     }
-    const int n1 = G > 1 ? 2 * (G - 1) : 0, n2 = G, nrow = G > 1 ? 3 * (G - 1) : 0;
+    const int n1 = G > 1 ? 2 * (G - 1) : 0, n2 = G, nrow = G > 1 ? 3 * G - 2 : 0;
     int t1, t2, trow;
     const int o1 = carry1 + block_exclusive_scan(n1, &t1);
     const int o2 = carry2 + block_exclusive_scan(n2, &t2);
@@ -1162,23 +1258,24 @@ __device__ void split_plan(const PrefillParams& p) {
       const int rd = p.slots.read[b], wr = p.slots.write[b];
       const int ckb = p.ckpt_idx ? p.slots.ckpt_start[b] : 0;
       const int nbase = (pre & ~(kChunk - 1)) - pre;
-      auto lo = [&](int g) { return g == 0 ? 0 : nbase + kChunk * m * g; };
-      auto hi = [&](int g) { return min(L, nbase + kChunk * m * (g + 1)); };
+      const int mm = max(m, 1);
+      auto lo = [&](int g) { return g == 0 ? 0 : nbase + kChunk * mm * g; };
+      auto hi = [&](int g) { return G == 1 ? L : min(L, nbase + kChunk * mm * (g + 1)); };
       auto put = [](int32_t* d, int a, int b_, int c, int e, int f, int g_, int h, int i) {
         d[0] = a; d[1] = b_; d[2] = c; d[3] = e; d[4] = f; d[5] = g_; d[6] = h; d[7] = i;
       };
       for (int g = 0; g <= G - 2; ++g) {
         const int a = lo(g), n = hi(g) - a;
-        put(p.seg1 + kSegWords * (o1 + 2 * g), tok0 + a, n, pre + a, cs + g * m, -1,
-            -2 - (row0 + G - 1 + g), 0, kSegOffset);
-        put(p.seg1 + kSegWords * (o1 + 2 * g + 1), tok0 + a, n, pre + a, cs + g * m, -1,
-            -2 - (row0 + 2 * (G - 1) + g), 0, kSegMap);
+        put(p.seg1 + kSegWords * (o1 + 2 * g), tok0 + a, n, pre + a, cs + g * mm, -1,
+            -2 - (row0 + G + g), 0, kSegOffset);
+        put(p.seg1 + kSegWords * (o1 + 2 * g + 1), tok0 + a, n, pre + a, cs + g * mm, -1,
+            -2 - (row0 + 2 * G - 1 + g), 0, kSegMap);
       }
       for (int g = 0; g <= G - 1; ++g) {
         const int a = lo(g), n = hi(g) - a;
         const int ck = p.ckpt_idx ? ckb + (pre + a) / p.ckpt_every - pre / p.ckpt_every : 0;
-        put(p.seg2 + kSegWords * (o2 + g), tok0 + a, n, pre + a, cs + g * m,
-            g == 0 ? rd : -2 - (row0 + g - 1), g == G - 1 ? wr : -1, ck, kSegNormal);
+        put(p.seg2 + kSegWords * (o2 + g), tok0 + a, n, pre + a, cs + g * mm,
+            G == 1 ? rd : -2 - (row0 + g), g == G - 1 ? wr : -1, ck, kSegNormal);
       }
     }
     carry1 += t1;
@@ -1197,7 +1294,7 @@ __device__ void split_plan(const PrefillParams& p) {
 __global__ __launch_bounds__(kPlanTile) void plan_kernel(const PrefillParams p) {
   plan_body(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs, p.num_chunk_slots,
             p.order, p.chunk_tab, (uint32_t*)p.zero_row);
-  if (p.split_m > 0) split_plan(p);
+  if (p.split_mode != kSplitOff) split_plan(p);
 }
 
 // start_{g+1} = start_g M_g + N_g for g = 0 .. G-2, 16 state rows of one
@@ -1240,7 +1337,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   auto state = [&](int row) { return p.ws_state + (int64_t)row * p.ws_state_stride + hoff; };
   // M_g into buffer X: 64 row pairs of 1 KiB, 16 per wave
   auto fetch = [&](int g, int X) {
-    const char* src = uniform_ptr(state(row0 + 2 * (G - 1) + g));
+    const char* src = uniform_ptr(state(row0 + 2 * G - 1 + g));
     const uint32_t dst = lds_addr(&sm.M[X][0][0]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1268,6 +1365,13 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   }
   *(f32x4*)&sm.S[r][c0] = i0;
   *(f32x4*)&sm.S[r][64 + c0] = i1;
+  // start_0 into the workspace: the second pass reads it there, never the
+  // caller's row, which that pass may overwrite
+  {
+    float* s0 = state(row0) + (int64_t)(16 * rb + r) * kDim;
+    *(f32x4*)(s0 + c0) = i0;
+    *(f32x4*)(s0 + 64 + c0) = i1;
+  }
   wait_loads();
   __syncthreads();
   for (int g = 0; g <= G - 2; ++g) {
@@ -1275,7 +1379,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
     if (g + 1 <= G - 2) fetch(g + 1, X ^ 1);
     // this lane's outputs: rows 4 gq + i, columns 32 wid + 16 t + n16; N_g is
     // added after the product, so its loads are in flight meanwhile
-    const float* Ng = state(row0 + G - 1 + g) + (int64_t)(16 * rb) * kDim + 32 * wid + n16;
+    const float* Ng = state(row0 + G + g) + (int64_t)(16 * rb) * kDim + 32 * wid + n16;
     float nv[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -1303,7 +1407,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
         acc[t] = mfma16x16x32(alo, bhi, acc[t]);
       }
     }
-    float* out = state(row0 + g) + (int64_t)(16 * rb) * kDim + 32 * wid + n16;  // start_{g+1}
+    float* out = state(row0 + g + 1) + (int64_t)(16 * rb) * kDim + 32 * wid + n16;  // start_{g+1}
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1323,15 +1427,26 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
 
 }  // namespace
 
+// The dynamic-LDS limit of a kernel is raised once per device (the
+// attribute belongs to the device's copy of the kernel); idempotent if two
+// threads race.
+static bool raise_lds_limit(const void* fn, int bytes, bool (&done)[kMaxDevices], hipError_t* err) {
+  const int dev = current_device();
+  if (dev >= 0 && dev < kMaxDevices && done[dev]) return true;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) {
+    *err = e;
+    return false;
+  }
+  if (dev >= 0 && dev < kMaxDevices) done[dev] = true;
+  return true;
+}
+
 template <int NW, bool OUT>
 hipError_t launch_rec(const PrefillParams& p, int64_t blocks, hipStream_t s) {
-  static bool attr_set = false;  // raised once per process and instance; idempotent if raced
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)rec_kernel<NW, OUT>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(RecSmem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static bool done[kMaxDevices] = {};
+  hipError_t e = hipSuccess;
+  if (!raise_lds_limit((const void*)rec_kernel<NW, OUT>, (int)sizeof(RecSmem), done, &e)) return e;
   rec_kernel<NW, OUT><<<(unsigned)blocks, NW * 64, sizeof(RecSmem), s>>>(p);
   return hipGetLastError();
 }
@@ -1339,24 +1454,21 @@ hipError_t launch_rec(const PrefillParams& p, int64_t blocks, hipStream_t s) {
 hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0 || num_chunk_slots <= 0) return hipSuccess;
-  if (p.split_m > 0 && (p.seg_cap1 <= 0 || p.seg_cap2 <= 0)) return hipErrorInvalidValue;
+  const bool split = p.split_mode != kSplitOff;
+  if (split && (p.seg_cap1 <= 0 || p.seg_cap2 <= 0)) return hipErrorInvalidValue;
   plan_kernel<<<1, kPlanTile, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   wy_kernel<<<(unsigned)(num_chunk_slots * p.H), kWyThreads, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Whole heads per workgroup (8 waves).  Narrower V-tiles (4, 2 or 1
-  // waves) add workgroups but not speed: each still walks every chunk of its
-  // sequence, and the per-chunk time is set by the chunk's dependency chain,
-  // which fewer waves only lengthen (measured: a 32k-token single sequence,
-  // 32 heads, takes 2.28 / 2.32 / 2.68 / 3.69 ms with 8 / 4 / 2 / 1 waves).
-  // GDN_PREFILL_TILE_WAVES = 1, 2, 4 or 8 selects one (tests, tuning).
-  int nw = 8;
-  if (const char* f = getenv("GDN_PREFILL_TILE_WAVES")) {
-    const int v = atoi(f);
-    if (v == 1 || v == 2 || v == 4 || v == 8) nw = v;
-  }
+  // Whole heads per workgroup (8 waves) by default.  Narrower V-tiles (4, 2
+  // or 1 waves) add workgroups but not speed: each still walks every chunk of
+  // its sequence, and the per-chunk time is set by the chunk's dependency
+  // chain, which fewer waves only lengthen (measured: a 32k-token single
+  // sequence, 32 heads, takes 2.28 / 2.32 / 2.68 / 3.69 ms with 8 / 4 / 2 / 1
+  // waves).
+  const int nw = p.tile_waves;
   auto rec = [&](const PrefillParams& q, int64_t items, bool out) {
     switch (nw * 2 + out) {
       case 17: return launch_rec<8, true>(q, items * p.H, s);
@@ -1366,10 +1478,11 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
       case 5: return launch_rec<2, true>(q, items * p.H * 4, s);
       case 4: return launch_rec<2, false>(q, items * p.H * 4, s);
       case 3: return launch_rec<1, true>(q, items * p.H * 8, s);
-      default: return launch_rec<1, false>(q, items * p.H * 8, s);
+      case 2: return launch_rec<1, false>(q, items * p.H * 8, s);
+      default: return hipErrorInvalidValue;
     }
   };
-  if (p.split_m <= 0) return rec(p, p.num_seqs, true);
+  if (!split) return rec(p, p.num_seqs, true);
   // sequence-parallel (its segment plan came with the launch plan): first
   // pass, scan of the segment maps, second pass
   PrefillParams p1 = p;
@@ -1377,13 +1490,8 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   p1.vcount = p.seg_counts;
   if ((e = rec(p1, p.seg_cap1, false)) != hipSuccess) return e;
   {
-    static bool attr_set = false;  // raised once per process; idempotent if raced
-    if (!attr_set) {
-      if ((e = hipFuncSetAttribute((const void*)seg_scan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)sizeof(ScanSmem))) != hipSuccess)
-        return e;
-      attr_set = true;
-    }
+    static bool done[kMaxDevices] = {};
+    if (!raise_lds_limit((const void*)seg_scan_kernel, (int)sizeof(ScanSmem), done, &e)) return e;
   }
   seg_scan_kernel<<<(unsigned)(((int64_t)p.num_seqs * p.H + 7) / 8 * 64), 256, sizeof(ScanSmem), s>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -44,13 +44,16 @@ def test_version(lib):
     assert b"gfx950" in lib.gdn_version()
 
 
-def dims(H=4, Hqk=2, K=128, V=128, scale=0.0):
-    return _lib.Dims(Hqk, H, K, V, scale)
+def dims(H=4, Hqk=2, K=128, V=128, scale=0.0, options=None):
+    return _lib.Dims(Hqk, H, K, V, scale, 0, C.pointer(options) if options is not None else None)
 
 
-def test_workspace_size(lib, monkeypatch):
-    monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")  # whole-sequence recurrence
-    d = dims()
+def split_opt(m):
+    return _lib.Options(prefill_split_chunks=m)
+
+
+def test_workspace_size(lib):
+    d = dims(options=split_opt(-1))  # whole-sequence recurrence
     a = lib.gdn_prefill_workspace_size(0, 1, C.byref(d))
     b = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
     c = lib.gdn_prefill_workspace_size(64 * 100, 300, C.byref(d))
@@ -66,51 +69,66 @@ def test_workspace_size(lib, monkeypatch):
     assert lib.gdn_prefill_workspace_size(64, 1, C.byref(bad)) == 0
 
 
-def test_workspace_size_sequence_parallel(lib, monkeypatch):
+def test_workspace_size_sequence_parallel(lib):
     """Splitting into segments of m chunks adds the records of both passes, the
     per-sequence scan records and up to 3 segment states per segment, with
     ceil(c / m) <= (T/64 + 2B + 1) / m + B segments in all."""
-    d = dims()  # H = 4: one sequence leaves the chip idle, so the default splits
-    monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")
-    whole = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d))
+    whole = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(dims(options=split_opt(-1))))
     al = lambda x: (x + 255) // 256 * 256
     for m in (4, 7):
-        monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", str(m))
         segs = 103 // m + 1
         extra = al(2 * segs * 32) + al(segs * 32) + al(16) + 256 + 3 * segs * 4 * 128 * 128 * 4
+        d = dims(options=split_opt(m))
         assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == extra
-    monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS")
-    # default: room for the segments of ANY call of at most these sizes, the
-    # smaller of 256/H + 256/H/16 + 1 + B' = 70 and (T/64 + 2B' + 1)/4 + B' = 26
-    # (B' = min(B, 64/H, T/896) = 1): m = 4 here
-    assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == \
-        al(52 * 32) + al(26 * 32) + al(16) + 256 + 78 * 4 * 128 * 128 * 4
-    # a batch that fills the chip does not split itself, but a smaller one
-    # within the same sizes may: min(256/32 + 0 + 1 + 2, 1005/4 + 2) = 11 segments
+    # default (the device plans from the lengths): room for the segments of
+    # ANY call of at most these sizes, min((T/64 + 2B' + 1)/4 + B', 512/H + B')
+    # with B' = min(B, 256/H): min(26, 129) = 26 here
+    for d in (dims(), dims(options=split_opt(0))):
+        assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == \
+            al(52 * 32) + al(26 * 32) + al(16) + 256 + 78 * 4 * 128 * 128 * 4
+    # 8 sequences x 32 heads fill 256 units once: min(1017/4 + 8, 16 + 8) = 24
+    # segments; 9 sequences do not split themselves, but a smaller batch within
+    # the same sizes may, so the room stays (with a 9-entry scan region)
+    big0 = dims(H=32, Hqk=32, options=split_opt(-1))
     big = dims(H=32, Hqk=32)
-    monkeypatch.setenv("GDN_PREFILL_SPLIT_CHUNKS", "0")
-    w0 = lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big))
-    monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS")
-    assert lib.gdn_prefill_workspace_size(64 * 1000, 8, C.byref(big)) - w0 == \
-        al(22 * 32) + al(11 * 32) + al(8 * 16) + 256 + 33 * 32 * 128 * 128 * 4
+    for B in (8, 9):
+        w0 = lib.gdn_prefill_workspace_size(64 * 1000, B, C.byref(big0))
+        assert lib.gdn_prefill_workspace_size(64 * 1000, B, C.byref(big)) - w0 == \
+            al(48 * 32) + al(24 * 32) + al(B * 16) + 256 + 72 * 32 * 128 * 128 * 4
+    # too few tokens for a 16-chunk sequence: no sequence-parallel room
+    assert lib.gdn_prefill_workspace_size(1023, 1, C.byref(dims())) == \
+        lib.gdn_prefill_workspace_size(1023, 1, C.byref(dims(options=split_opt(-1))))
 
 
 @pytest.mark.parametrize("H", [1, 4, 32, 128])
-def test_workspace_size_monotone(lib, monkeypatch, H):
+@pytest.mark.parametrize("split", [0, 3])
+def test_workspace_size_monotone(lib, H, split):
     """A workspace sized for (T, B) serves every call with fewer tokens or
-    sequences: the size never drops as either grows (the sequence-parallel
-    choice depends on both)."""
-    monkeypatch.delenv("GDN_PREFILL_SPLIT_CHUNKS", raising=False)
-    d = dims(H=H, Hqk=1)
+    sequences: the size never drops as either grows (whether the batch may
+    split depends on both)."""
+    d = dims(H=H, Hqk=1, options=split_opt(split))
     size = lambda T, B: lib.gdn_prefill_workspace_size(T, B, C.byref(d))  # noqa: E731
-    Ts = [0, 1, 63, 64, 65, 640, 1000, 1024, 4000, 8191, 8192, 30000, 70000, 200000]
-    Bs = [1, 2, 3, 7, 16, 64, 65, 300]
+    Ts = [0, 1, 63, 64, 65, 640, 1000, 1023, 1024, 4000, 8191, 8192, 30000, 70000, 200000]
+    Bs = [1, 2, 3, 7, 8, 9, 16, 64, 65, 256, 257, 300]
     for B in Bs:
         sizes = [size(T, B) for T in Ts]
         assert sizes == sorted(sizes), (H, B, sizes)
     for T in Ts:
         sizes = [size(T, B) for B in Bs]
         assert sizes == sorted(sizes), (H, T, sizes)
+
+
+@pytest.mark.parametrize("field,value", [("prefill_split_chunks", -2), ("prefill_tile_waves", 3),
+                                         ("prefill_tile_waves", 16), ("decode_waves", 1),
+                                         ("decode_waves", 32), ("decode_stream_per_cu", -2),
+                                         ("decode_stream_grid", -1)])
+def test_bad_options(lib, field, value):
+    o = _lib.Options()
+    setattr(o, field, value)
+    d = dims(options=o)
+    assert lib.gdn_prefill_workspace_size(64, 1, C.byref(d)) == 0
+    assert _prefill_paged(lib, d) == -1
+    assert b"options" in lib.gdn_last_error()
 
 
 def _prefill_paged(lib, d, page_size=128, stride=4 * 128 * 128, ws=1 << 30, pool=1, cu=1,

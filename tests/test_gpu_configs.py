@@ -146,11 +146,15 @@ def test_config3_long_prefill_full():
             assert (ck[r].view(torch.int32) == workloads.NAN_BITS).all(), f"checkpoint {r} written"
 
 
-def test_config4_hybrid_layer():
+@pytest.mark.parametrize("qk_heads", [32, 16])
+def test_config4_hybrid_layer(qk_heads):
     """One layer of the hybrid step with slots derived once: sampled sequences
-    and heads against the oracle, write sets on the whole pool."""
+    and heads against the oracle, write sets on the whole pool.  With 16 q/k
+    heads the prefill kernels place the v-heads in q/k-head pairs; the sampled
+    heads then cover both v-heads of a pair and both halves of the q/k heads."""
     m = lib()
-    c = workloads.config4(device=DEV, layers=(0,))
+    c = workloads.config4(device=DEV, layers=(0,), qk_heads=qk_heads)
+    group = c["H"] // c["Hqk"]
     pool = c["pool"]
     pre, dec = c["layers"][0]["prefill"], c["layers"][0]["decode"]
     ps = c["page_size"]
@@ -161,7 +165,7 @@ def test_config4_hybrid_layer():
                                  pre["page_indptr"].tolist(), pre["last_page_len"].tolist(), ps)
     for name in sl_p._fields:
         assert getattr(sl_p, name).tolist() == ref_p[name], name
-    heads = [5, 26]
+    heads = [5, 26] if group == 1 else [5, 10, 19, 26]
     seqs_p = [0, 9, 31, 33]        # includes one padded (zero-length) sequence
     seqs_d = list(range(0, 528, 17))
     rows_in_p = rows_of(pool, [pre["read_rows"][b] for b in seqs_p if pre["new"][b] > 0], heads)
@@ -194,7 +198,7 @@ def test_config4_hybrid_layer():
     assert changed_rows(before, pool) == sorted(expect)
     # prefill oracle on sampled sequences and heads
     toks, ncu, nidx, nptr, nlpl = seq_slice(pre, seqs_p)
-    hs = head_slice(pre, heads, 1)
+    hs = head_slice(pre, heads, group)
     sub = {k: v[toks] for k, v in hs.items()}
     o_ref, writes, _ = ogdn.prefill_paged(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
                                           ncu, RowView(rows_in_p), nidx, nptr, nlpl, ps)
@@ -202,7 +206,7 @@ def test_config4_hybrid_layer():
     for r, s in writes.items():
         check_state(pool[r][heads], s, f"prefill page {r}")
     # decode oracle on sampled sequences and heads
-    hd = head_slice(dec, heads, 1)
+    hd = head_slice(dec, heads, group)
     res = ogdn.decode(hd["q"][seqs_d], hd["k"][seqs_d], hd["v"][seqs_d], hd["g"][seqs_d],
                       hd["beta"][seqs_d], initial_state=RowView(rows_in_d),
                       initial_state_indices=[dslots["initial_state_indices"][b] for b in seqs_d],

@@ -6,7 +6,6 @@ the eager result bit for bit (outputs and the whole pool).  The library
 launches kernels only (no memset, allocation or host synchronization inside a
 call), which is what makes the calls capturable."""
 
-import os
 
 import pytest
 import torch
@@ -78,47 +77,50 @@ def test_graph_hybrid_layer():
                      (o_pre_e, o_dec_e, pool_e), ("o prefill", "o decode", "pool"))
 
 
-def test_graph_sequence_parallel_prefill():
+@pytest.mark.parametrize("split,total,splits", [(3, 1000, (131, 400, 640)),
+                                                (0, 3000, (131, 400, 2640))])
+def test_graph_sequence_parallel_prefill(split, total, splits):
+    """A sequence-parallel prefill captured and replayed: forced segments of 3
+    chunks, and the plan the device picks from the lengths (a 2240-token
+    middle piece)."""
     m = lib()
-    os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = "3"
-    try:
-        c = cuda(workloads.config3(heads=2, total=1000, splits=(131, 400, 640), every_n=128,
-                                   num_rows=3, g_scale=0.1))
-        call = c["calls"][2]  # a middle piece: reads and writes the slot, checkpoints inside
-        T = call["q"].shape[0]
-        ws = torch.empty(m.prefill_workspace_size(T, 1, 2, 2), dtype=torch.uint8, device=DEV)
-        ckpt0 = workloads.nan_pool(1000 // 128, 2, 128, 128, device=DEV)
-        slot0 = c["pool"]
-        slot0.zero_()
-        slot0[c["slot"]].normal_(0, 0.05)
+    o3 = m.Options(prefill_split_chunks=split)
+    c = cuda(workloads.config3(heads=2, total=total, splits=splits, every_n=128,
+                               num_rows=3, g_scale=0.1))
+    call = c["calls"][2]  # a middle piece: reads and writes the slot, checkpoints inside
+    T = call["q"].shape[0]
+    ws = torch.empty(m.prefill_workspace_size(T, 1, 2, 2, options=o3), dtype=torch.uint8,
+                     device=DEV)
+    ckpt0 = workloads.nan_pool(total // 128, 2, 128, 128, device=DEV)
+    slot0 = c["pool"]
+    slot0.zero_()
+    slot0[c["slot"]].normal_(0, 0.05)
 
-        def run(slot, ckpt, o):
-            m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
-                      call["cu_seqlens"], initial_state=slot,
-                      state_indices=call["state_indices"], output_state=slot,
-                      output_state_indices=call["output_state_indices"],
-                      output_final_state=True, state_checkpoints=ckpt,
-                      checkpoint_state_indices=c["checkpoint_state_indices"],
-                      checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                      prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=128,
-                      workspace=ws, out=o)
+    def run(slot, ckpt, o):
+        m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
+                  call["cu_seqlens"], initial_state=slot,
+                  state_indices=call["state_indices"], output_state=slot,
+                  output_state_indices=call["output_state_indices"],
+                  output_final_state=True, state_checkpoints=ckpt,
+                  checkpoint_state_indices=c["checkpoint_state_indices"],
+                  checkpoint_cu_starts=call["checkpoint_cu_starts"],
+                  prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=128,
+                  workspace=ws, out=o, options=o3)
 
-        slot_e, ckpt_e = slot0.clone(), ckpt0.clone()
-        o_e = torch.empty(T, 2, 128, dtype=torch.bfloat16, device=DEV)
-        run(slot_e, ckpt_e, o_e)
-        torch.cuda.synchronize()
+    slot_e, ckpt_e = slot0.clone(), ckpt0.clone()
+    o_e = torch.empty(T, 2, 128, dtype=torch.bfloat16, device=DEV)
+    run(slot_e, ckpt_e, o_e)
+    torch.cuda.synchronize()
 
-        slot_g, ckpt_g = slot0.clone(), ckpt0.clone()
-        o_g = torch.empty_like(o_e)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run(slot_g, ckpt_g, o_g)
+    slot_g, ckpt_g = slot0.clone(), ckpt0.clone()
+    o_g = torch.empty_like(o_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(slot_g, ckpt_g, o_g)
 
-        def reset():
-            slot_g.copy_(slot0)
-            ckpt_g.copy_(ckpt0)
+    def reset():
+        slot_g.copy_(slot0)
+        ckpt_g.copy_(ckpt0)
 
-        replay_and_check(g, reset, (o_g, ckpt_g, slot_g), (o_e, ckpt_e, slot_e),
-                         ("o", "checkpoints", "slot rows"))
-    finally:
-        os.environ.pop("GDN_PREFILL_SPLIT_CHUNKS", None)
+    replay_and_check(g, reset, (o_g, ckpt_g, slot_g), (o_e, ckpt_e, slot_e),
+                     ("o", "checkpoints", "slot rows"))

@@ -1,0 +1,115 @@
+"""The sequence-parallel plan the device builds, read back from the workspace.
+
+White-box: the workspace regions are located as the library lays them out
+(per-sequence rows, launch order, zero row, chunk table, intra-chunk records,
+then the segment records of both passes, the scan records, the counts and the
+segment states, each region 256-byte aligned).  For forced and device-chosen
+segment lengths the records must:
+  * cover every sequence's new tokens exactly, in order, in both passes;
+  * never read a caller row in the first pass (zero or identity starts) and,
+    for a sequence cut in two or more segments, never read one in the second
+    pass either (segment 0 reads the scan's copy of the initial state), so no
+    launch both reads and writes a caller row;
+  * write the caller's final row only from the last segment;
+  * use workspace state rows inside the room the size query reserved.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.test_gpu_small import lib, make_case, opts
+
+pytestmark = pytest.mark.gpu
+
+REC_BYTES = 10240 + 1024  # intra-chunk record per (chunk slot, v-head)
+
+
+def al(x):
+    return (x + 255) // 256 * 256
+
+
+def plan_regions(T, B, H, split, m_forced=0):
+    """Byte offsets of the segment regions (mirrors the workspace layout)."""
+    nc = T // 64 + 2 * B + 1
+    if m_forced > 0:
+        segs = nc // m_forced + B
+    else:
+        segs = min(nc // 4 + B, 512 // H + B)
+    off = al(5 * B * 4) + al(B * 4) + 256 + al(nc * 16) + al(nc * H * 10240) + al(nc * H * 1024)
+    seg1 = off
+    off += al(2 * segs * 32)
+    seg2 = off
+    off += al(segs * 32)
+    scan = off
+    off += al(B * 16)
+    counts = off
+    return dict(seg1=seg1, seg2=seg2, scan=scan, counts=counts, cap=segs)
+
+
+def read_i32(ws, off, n):
+    return ws[off:off + 4 * n].view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("split", [2, 0])
+def test_plan_records(split):
+    m = lib()
+    # ragged lengths with long sequences, 2 heads: the device plan splits
+    prefix = [37, 0, 256, 1000, 5]
+    new = [3000, 2500, 60, 4100, 0]
+    H = 2
+    pre, pool = make_case(prefix, new, ps=128, H=H, Hqk=1, seed=81, g_scale=0.1)
+    T, B = sum(new), len(new)
+    o = opts(prefill_split_chunks=split)
+    ws = torch.zeros(m.prefill_workspace_size(T, B, H, 1, options=o), dtype=torch.uint8,
+                     device="cuda")
+    sl = m.prefill_slots(pre["cu_seqlens"], pre["page_indices"], pre["page_indptr"],
+                         pre["last_page_len"], pre["page_size"])
+    m.prefill_paged(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], pre["cu_seqlens"], pool,
+                    pre["page_indices"], pre["page_indptr"], pre["page_size"],
+                    pre["last_page_len"], slots=sl, workspace=ws, options=o)
+    torch.cuda.synchronize()
+    reg = plan_regions(T, B, H, split, m_forced=split)
+    n1, n2 = read_i32(ws, reg["counts"], 2)
+    rec1 = read_i32(ws, reg["seg1"], 8 * n1).reshape(-1, 8)
+    rec2 = read_i32(ws, reg["seg2"], 8 * n2).reshape(-1, 8)
+    scan = read_i32(ws, reg["scan"], 4 * B).reshape(-1, 4)
+    cu = pre["cu_seqlens"].tolist()
+    rd = sl.state_indices.tolist()
+    wr = sl.output_state_indices.tolist()
+    assert n2 <= reg["cap"] and n1 <= 2 * reg["cap"]
+    rows = 0
+    i1 = i2 = 0
+    split_any = False
+    for b in range(B):
+        G, row0 = int(scan[b][0]), int(scan[b][1])
+        L = cu[b + 1] - cu[b]
+        if L == 0:
+            assert G == 0
+            continue
+        assert G >= 1
+        mine2 = rec2[i2:i2 + G]
+        i2 += G
+        # second pass covers the tokens in order
+        assert mine2[0][0] == cu[b] and sum(int(r[1]) for r in mine2) == L
+        for x, y in zip(mine2, mine2[1:]):
+            assert y[0] == x[0] + x[1]
+        assert [int(r[5]) for r in mine2] == [-1] * (G - 1) + [wr[b]]
+        if G == 1:
+            assert mine2[0][4] == rd[b]  # a whole sequence reads its own row
+            continue
+        split_any = True
+        assert row0 == rows
+        rows += 3 * G - 2
+        # every second-pass start is a workspace state: start_g at row0 + g
+        assert [int(r[4]) for r in mine2] == [-2 - (row0 + g) for g in range(G)]
+        mine1 = rec1[i1:i1 + 2 * (G - 1)]
+        i1 += 2 * (G - 1)
+        assert (mine1[:, 4] == -1).all()          # zero / identity starts
+        assert (mine1[:, 5] <= -2).all()          # workspace results only
+        assert sorted(-2 - mine1[:, 5].astype(int)) == list(range(row0 + G, row0 + 3 * G - 2))
+    assert i1 == n1 and i2 == n2
+    assert rows <= 3 * reg["cap"]
+    assert split_any, "the plan cut no sequence"
+    print(f"split {split}: {n1} first-pass and {n2} second-pass records; segments per "
+          f"sequence {[int(x[0]) for x in scan]}")

@@ -5,8 +5,6 @@ sequence-parallel splits drawn per case.  The same parity bar as every other
 GPU test: outputs and states within tolerance, page-write set and untouched
 rows bit for bit."""
 
-import os
-
 import numpy as np
 import pytest
 
@@ -30,8 +28,8 @@ def draw_case(seed):
             prefix[b] = 1  # every sequence holds a token (one page)
     g_scale = float(rng.choice([0.0, 0.1, 1.0]))
     bf16 = bool(rng.random() < 0.3)
-    waves = str(int(rng.choice([8, 8, 4, 2])))
-    split = rng.choice([None, None, "1", "2", "3"])
+    waves = int(rng.choice([8, 8, 4, 2]))
+    split = int(rng.choice([0, 0, -1, 1, 2, 3]))
     return dict(prefix=prefix, new=new, ps=ps, H=H, Hqk=Hqk, g_scale=g_scale, bf16=bf16,
                 waves=waves, split=split)
 
@@ -39,25 +37,39 @@ def draw_case(seed):
 @pytest.mark.parametrize("seed", range(16))
 def test_random_paged_prefill(seed):
     import torch
+
+    from tests.test_gpu_small import opts
     c = draw_case(seed)
-    env = {"GDN_PREFILL_TILE_WAVES": c["waves"]}
-    if c["split"] is not None:
-        env["GDN_PREFILL_SPLIT_CHUNKS"] = str(c["split"])
-    old = {k: os.environ.get(k) for k in env}
-    os.environ.update(env)
-    try:
-        pre, pool = make_case(c["prefix"], c["new"], ps=c["ps"], H=c["H"], Hqk=c["Hqk"],
-                              seed=seed, g_scale=c["g_scale"])
-        if c["bf16"]:
-            pool = pool.to(torch.bfloat16)
-        _, _, err = check_paged_prefill(pre, pool)
-        print(f"case {seed}: {c} worst state rel {err:.2e}")
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+    pre, pool = make_case(c["prefix"], c["new"], ps=c["ps"], H=c["H"], Hqk=c["Hqk"],
+                          seed=seed, g_scale=c["g_scale"])
+    if c["bf16"]:
+        pool = pool.to(torch.bfloat16)
+    o = opts(prefill_tile_waves=c["waves"], prefill_split_chunks=c["split"])
+    _, _, err = check_paged_prefill(pre, pool, options=o)
+    print(f"case {seed}: {c} worst state rel {err:.2e}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_paged_prefill_grouped_heads(seed):
+    """Random draws on head layouts whose v-heads the prefill kernels place in
+    q/k-head groups (16 on 8, 32 on 16), shorter sequences."""
+    import torch
+
+    from tests.test_gpu_small import opts
+    c = draw_case(100 + seed)
+    c["H"], c["Hqk"] = [(16, 8), (32, 16)][seed % 2]
+    c["prefix"] = [min(x, 300) for x in c["prefix"]][:4]
+    c["new"] = [min(x, 260) for x in c["new"]][:4]
+    for b in range(len(c["new"])):
+        if c["prefix"][b] + c["new"][b] == 0:
+            c["prefix"][b] = 1
+    pre, pool = make_case(c["prefix"], c["new"], ps=c["ps"], H=c["H"], Hqk=c["Hqk"],
+                          seed=seed, g_scale=c["g_scale"])
+    if c["bf16"]:
+        pool = pool.to(torch.bfloat16)
+    o = opts(prefill_tile_waves=c["waves"], prefill_split_chunks=c["split"])
+    _, _, err = check_paged_prefill(pre, pool, options=o)
+    print(f"grouped case {seed}: {c} worst state rel {err:.2e}")
 
 
 def draw_general(seed):

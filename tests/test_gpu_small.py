@@ -25,11 +25,17 @@ def lib():
     return m
 
 
-def run_prefill_paged(pre, pool, slots=None, scale=None):
+def opts(**kw):
+    """Launch choices of a call (every field not given: the default)."""
+    return lib().Options(**kw)
+
+
+def run_prefill_paged(pre, pool, slots=None, scale=None, options=None):
     m = lib()
     return m.prefill_paged(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"],
                            pre["cu_seqlens"], pool, pre["page_indices"], pre["page_indptr"],
-                           pre["page_size"], pre["last_page_len"], slots=slots, scale=scale)
+                           pre["page_size"], pre["last_page_len"], slots=slots, scale=scale,
+                           options=options)
 
 
 def state_dtype_of(pool):
@@ -44,12 +50,12 @@ def oracle_prefill_paged(pre, pool_rows, state_dtype="fp32"):
                               state_dtype=state_dtype)
 
 
-def check_paged_prefill(pre, pool):
+def check_paged_prefill(pre, pool, options=None):
     """Run GPU and oracle on the same inputs; check outputs, written states,
     the write set and every untouched row bit for bit."""
     rows_in = pool_rows_cpu(pool, [r for r in pre["read_rows"]])
     before = pool.clone()
-    o = run_prefill_paged(pre, pool)
+    o = run_prefill_paged(pre, pool, options=options)
     torch.cuda.synchronize()
     o_ref, writes, _ = oracle_prefill_paged(pre, rows_in, state_dtype_of(pool))
     check_outputs(o, o_ref)
@@ -232,32 +238,29 @@ def test_decode_every_workgroup_width(waves):
     default grid, and a grid of 5 workgroups so each walks ~10 pairs through
     its prefetch pipeline."""
     m = lib()
-    env = {"stream": {"GDN_DECODE_STREAM": "6"},
-           "stream-grid-5": {"GDN_DECODE_STREAM_GRID": "5"}}.get(waves, {"GDN_DECODE_WAVES": waves})
-    os.environ.update(env)
-    try:
-        c = cuda(workloads.config2(num_seqs=12, qk_heads=2, v_heads=4, num_pages=12 * 32,
-                                   new_page_seqs=4, seed=40 + len(waves)))
-        dec = c["decode"]
-        for pool in (c["pool"], c["pool"].to(torch.bfloat16)):
-            rows_in = pool_rows_cpu(pool, dec["read_rows"])
-            before = pool.clone()
-            o = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
-                               dec["page_indices"], dec["page_indptr"], 1024, dec["last_page_len"])
-            torch.cuda.synchronize()
-            o_ref, writes, _ = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
-                                                 dec["g"].cpu(), dec["beta"].cpu(),
-                                                 RowView(rows_in), dec["page_indices"].cpu(),
-                                                 dec["page_indptr"].cpu(),
-                                                 dec["last_page_len"].cpu(),
-                                                 state_dtype=state_dtype_of(pool))
-            check_outputs(o, o_ref)
-            assert changed_rows(before, pool) == sorted(writes)
-            for r, s in writes.items():
-                check_state(pool[r], s)
-    finally:
-        for k in env:
-            del os.environ[k]
+    o_kw = {"stream": dict(decode_stream_per_cu=6),
+            "stream-grid-5": dict(decode_stream_grid=5)}.get(waves, dict(decode_waves=int(waves) if waves.isdigit() else 0))
+    options = opts(**o_kw)
+    c = cuda(workloads.config2(num_seqs=12, qk_heads=2, v_heads=4, num_pages=12 * 32,
+                               new_page_seqs=4, seed=40 + len(waves)))
+    dec = c["decode"]
+    for pool in (c["pool"], c["pool"].to(torch.bfloat16)):
+        rows_in = pool_rows_cpu(pool, dec["read_rows"])
+        before = pool.clone()
+        o = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
+                           dec["page_indices"], dec["page_indptr"], 1024, dec["last_page_len"],
+                           options=options)
+        torch.cuda.synchronize()
+        o_ref, writes, _ = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
+                                             dec["g"].cpu(), dec["beta"].cpu(),
+                                             RowView(rows_in), dec["page_indices"].cpu(),
+                                             dec["page_indptr"].cpu(),
+                                             dec["last_page_len"].cpu(),
+                                             state_dtype=state_dtype_of(pool))
+        check_outputs(o, o_ref)
+        assert changed_rows(before, pool) == sorted(writes)
+        for r, s in writes.items():
+            check_state(pool[r], s)
 
 
 @pytest.mark.parametrize("idx_dtype", [torch.int32, torch.int64])
@@ -377,126 +380,157 @@ def test_split_invariance_on_gpu():
         check_state(pool[r], s, f"page {r}")
 
 
+def check_sliced_general(H=2, Hqk=None, N=128, total=1000, splits=(131, 400, 640), g_scale=0.1,
+                         options=None, state_dtype=torch.float32, seed=3, idx_dtype=torch.int32,
+                         in_place_default=False):
+    """A long sequence through the slot-argument call in pieces (state kept in
+    one slot row, read and written in place), checkpoints every N tokens into
+    a separate NaN-filled buffer with every other row -1; each piece against
+    the oracle, then the checkpoint rows.  ``in_place_default`` passes no
+    output_state_indices (the write row is then the read row).  Returns the
+    worst state error."""
+    m = lib()
+    sd = "bf16" if state_dtype == torch.bfloat16 else "fp32"
+    c = cuda(workloads.config3(heads=H, qk_heads=Hqk, total=total, splits=splits, every_n=N,
+                               num_rows=3, g_scale=g_scale, seed=seed))
+    slot_pool = c["pool"].to(state_dtype)
+    n_ck = total // N
+    ckpt = workloads.nan_pool(max(n_ck, 1), H, 128, 128, device=DEV).to(state_dtype)
+    ckpt0 = ckpt.clone()
+    ck_rows = c["checkpoint_state_indices"].to(idx_dtype)
+    ref_slot = np.zeros((3, H, 128, 128))
+    ref_ck = {}
+    worst = 0.0
+    for call in c["calls"]:
+        cast = {k: call[k].to(idx_dtype) for k in ("state_indices", "output_state_indices",
+                                                   "prefix_lens", "checkpoint_cu_starts")}
+        if in_place_default and call["start"] > 0:
+            wr = None  # the read row, which is the slot
+        else:
+            wr = cast["output_state_indices"]
+        o = m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"], call["cu_seqlens"],
+                      initial_state=slot_pool, state_indices=cast["state_indices"],
+                      output_state=slot_pool, output_state_indices=wr,
+                      output_final_state=True, state_checkpoints=ckpt,
+                      checkpoint_state_indices=ck_rows,
+                      checkpoint_cu_starts=cast["checkpoint_cu_starts"],
+                      prefix_lens=cast["prefix_lens"], checkpoint_every_n_tokens=N,
+                      options=options)
+        torch.cuda.synchronize()
+        res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(), call["g"].cpu(),
+                           call["beta"].cpu(), call["cu_seqlens"].cpu(), initial_state=ref_slot,
+                           state_indices=call["state_indices"].tolist(), output_final_state=True,
+                           output_state_indices=call["output_state_indices"].tolist(),
+                           checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
+                           checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
+                           prefix_lens=call["prefix_lens"].tolist(), checkpoint_every_n_tokens=N,
+                           shared_pool=False, state_dtype=sd)
+        check_outputs(o, res.o)
+        ref_slot = ogdn.apply_writes(ref_slot, res.final)
+        ref_ck.update(res.checkpoints)
+        worst = max(worst, check_state(slot_pool[c["slot"]], ref_slot[c["slot"]], "slot"))
+    got = [r for r in range(n_ck) if torch.isfinite(ckpt[r].float()).all()]
+    assert got == sorted(ref_ck) == [r for r in range(n_ck) if r % 2 == 0]
+    for r, st in ref_ck.items():
+        worst = max(worst, check_state(ckpt[r], st, f"checkpoint {r}"))
+    # odd rows (-1 entries) keep their NaN bits
+    assert changed_rows(ckpt0, ckpt) == [r for r in range(n_ck) if r % 2 == 0]
+    return worst
+
+
 @pytest.mark.parametrize("waves", [8, 4, 2, 1])
 def test_prefill_every_tile_width(waves):
     """The recurrence kernel in each of its V-tile widths (8, 4, 2 or 1 waves
-    per workgroup, forced): ragged sequences, GQA, slow decay, and a general
-    call with checkpoints."""
-    os.environ["GDN_PREFILL_TILE_WAVES"] = str(waves)
-    try:
-        pre, pool = make_case([0, 37, 128, 1], [130, 1, 64, 250], H=4, Hqk=2, seed=7, g_scale=0.3)
-        _, _, err = check_paged_prefill(pre, pool)
-        m = lib()
-        H = 2
-        N = 128
-        c = cuda(workloads.config3(heads=H, total=600, splits=(131, 400), every_n=N, num_rows=3))
-        ckpt = workloads.nan_pool(600 // N, H, 128, 128, device=DEV)
-        ref_slot = np.zeros((3, H, 128, 128))
-        ref_ck = {}
-        for call in c["calls"]:
-            o = m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
-                          call["cu_seqlens"], initial_state=c["pool"],
-                          state_indices=call["state_indices"], output_state=c["pool"],
-                          output_state_indices=call["output_state_indices"],
-                          output_final_state=True, state_checkpoints=ckpt,
-                          checkpoint_state_indices=c["checkpoint_state_indices"],
-                          checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                          prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=N)
-            torch.cuda.synchronize()
-            res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(), call["g"].cpu(),
-                               call["beta"].cpu(), call["cu_seqlens"].cpu(), initial_state=ref_slot,
-                               state_indices=call["state_indices"].tolist(), output_final_state=True,
-                               output_state_indices=call["output_state_indices"].tolist(),
-                               checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
-                               checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
-                               prefix_lens=call["prefix_lens"].tolist(), checkpoint_every_n_tokens=N,
-                               shared_pool=False)
-            check_outputs(o, res.o)
-            ref_slot = ogdn.apply_writes(ref_slot, res.final)
-            ref_ck.update(res.checkpoints)
-            check_state(c["pool"][c["slot"]], ref_slot[c["slot"]], "slot")
-        for r, st in ref_ck.items():
-            check_state(ckpt[r], st, f"checkpoint {r}")
-        print(f"{waves} waves per workgroup: worst paged state rel {err:.2e}")
-    finally:
-        del os.environ["GDN_PREFILL_TILE_WAVES"]
+    per workgroup): ragged sequences, GQA, slow decay, and a general call with
+    checkpoints."""
+    o = opts(prefill_tile_waves=waves, prefill_split_chunks=-1)
+    pre, pool = make_case([0, 37, 128, 1], [130, 1, 64, 250], H=4, Hqk=2, seed=7, g_scale=0.3)
+    _, _, err = check_paged_prefill(pre, pool, options=o)
+    check_sliced_general(H=2, N=128, total=600, splits=(131, 400), g_scale=1.0, options=o)
+    print(f"{waves} waves per workgroup: worst paged state rel {err:.2e}")
 
 
 @pytest.mark.parametrize("m,waves", [(1, 8), (2, 8), (3, 8), (5, 8), (2, 4)])
 def test_prefill_sequence_parallel(m, waves):
     """The sequence-parallel recurrence forced with segments of m chunks:
-    segment 0 for real, the middle segments' offsets (zero start) and
-    transitions (identity start, v = 0), the scan of the segment maps and the
-    second pass from the scanned starts.  Ragged paged sequences with GQA and
-    slow decay (so start states matter across segments), then a sliced long
-    sequence through the general call with checkpoints inside and at the ends
-    of chunks."""
-    os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = str(m)
-    os.environ["GDN_PREFILL_TILE_WAVES"] = str(waves)
-    try:
-        pre, pool = make_case([0, 37, 128, 1000], [700, 1, 64, 900], ps=128, H=4, Hqk=2,
-                              seed=11 + m, g_scale=0.1)
-        _, _, err = check_paged_prefill(pre, pool)
-        mod = lib()
-        H = 2
-        for N in (100, 128):
-            c = cuda(workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N,
-                                       num_rows=3, g_scale=0.1))
-            ckpt = workloads.nan_pool(1000 // N, H, 128, 128, device=DEV)
-            ref_slot = np.zeros((3, H, 128, 128))
-            ref_ck = {}
-            for call in c["calls"]:
-                o = mod.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
-                                call["cu_seqlens"], initial_state=c["pool"],
-                                state_indices=call["state_indices"], output_state=c["pool"],
-                                output_state_indices=call["output_state_indices"],
-                                output_final_state=True, state_checkpoints=ckpt,
-                                checkpoint_state_indices=c["checkpoint_state_indices"],
-                                checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                                prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=N)
-                torch.cuda.synchronize()
-                res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(),
-                                   call["g"].cpu(), call["beta"].cpu(), call["cu_seqlens"].cpu(),
-                                   initial_state=ref_slot,
-                                   state_indices=call["state_indices"].tolist(),
-                                   output_final_state=True,
-                                   output_state_indices=call["output_state_indices"].tolist(),
-                                   checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
-                                   checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
-                                   prefix_lens=call["prefix_lens"].tolist(),
-                                   checkpoint_every_n_tokens=N, shared_pool=False)
-                check_outputs(o, res.o)
-                ref_slot = ogdn.apply_writes(ref_slot, res.final)
-                ref_ck.update(res.checkpoints)
-                check_state(c["pool"][c["slot"]], ref_slot[c["slot"]], "slot")
-            got = [r for r in range(1000 // N) if torch.isfinite(ckpt[r]).all()]
-            assert got == sorted(ref_ck)
-            for r, st in ref_ck.items():
-                check_state(ckpt[r], st, f"checkpoint {r}")
-        print(f"segments of {m} chunks, {waves} waves: worst paged state rel {err:.2e}")
-    finally:
-        os.environ.pop("GDN_PREFILL_SPLIT_CHUNKS", None)
-        os.environ.pop("GDN_PREFILL_TILE_WAVES", None)
+    the segments' offsets (zero start) and transitions (identity start, v =
+    0), the scan of the segment maps and the second pass from the scanned
+    starts.  Ragged paged sequences with GQA and slow decay (so start states
+    matter across segments), then a sliced long sequence through the general
+    call with checkpoints inside and at the ends of chunks."""
+    o = opts(prefill_split_chunks=m, prefill_tile_waves=waves)
+    pre, pool = make_case([0, 37, 128, 1000], [700, 1, 64, 900], ps=128, H=4, Hqk=2,
+                          seed=11 + m, g_scale=0.1)
+    _, _, err = check_paged_prefill(pre, pool, options=o)
+    for N in (100, 128):
+        check_sliced_general(H=2, N=N, options=o)
+    print(f"segments of {m} chunks, {waves} waves: worst paged state rel {err:.2e}")
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_sequence_parallel_rows_read_and_written(m):
+    """Rows the second pass both reads and writes, under forced segments:
+    a paged prefix ending inside a page (37 of 128 tokens) whose page a later
+    segment checkpoints, next to a page-aligned prefix whose read page is
+    outside the call's write set; and the slot-argument call with no
+    output_state_indices, which updates each read row in place."""
+    o = opts(prefill_split_chunks=m)
+    pre, pool = make_case([37, 1, 256, 130], [700, 400, 300, 126], ps=128, H=2, Hqk=1,
+                          seed=60 + m, g_scale=0.1)
+    _, writes, err = check_paged_prefill(pre, pool, options=o)
+    read_rows = [r for r in pre["read_rows"] if r >= 0]
+    assert read_rows[0] in writes and read_rows[1] in writes  # read pages re-stored by later segments
+    worst = check_sliced_general(H=2, N=100, options=o, in_place_default=True)
+    print(f"segments of {m}: worst state rel {err:.2e} / {worst:.2e}")
+
+
+# ---- v-heads placed on the XCDs in q/k-head groups: H a multiple of 8 H / Hqk
+
+@pytest.mark.parametrize("H,Hqk,split,waves", [(16, 8, -1, 8), (16, 8, 2, 8), (32, 16, -1, 8),
+                                               (32, 16, 3, 8), (32, 16, -1, 4), (16, 8, 0, 8)])
+def test_prefill_gqa_head_placement(H, Hqk, split, waves):
+    """Head layouts where the recurrence and intra-chunk workgroups map block
+    indices to v-heads in q/k-head groups (H a multiple of 8 H / Hqk): every
+    head against the oracle, whole sequences and forced segments, a tile
+    width below whole heads, and the device-planned split (split 0)."""
+    o = opts(prefill_split_chunks=split, prefill_tile_waves=waves)
+    pre, pool = make_case([0, 37, 1000], [700, 190, 400], ps=128, H=H, Hqk=Hqk,
+                          seed=H + Hqk + split, g_scale=0.1)
+    _, writes, err = check_paged_prefill(pre, pool, options=o)
+    assert len(writes) >= 6
+    print(f"H={H} Hqk={Hqk} split {split} waves {waves}: worst state rel {err:.2e}")
+
+
+@pytest.mark.parametrize("H,Hqk,split", [(16, 8, -1), (32, 16, 2)])
+def test_general_prefill_gqa_head_placement(H, Hqk, split):
+    """The slot-argument call with interior checkpoints (every 100 tokens) on
+    the grouped head placement, int64 rows."""
+    err = check_sliced_general(H=H, Hqk=Hqk, N=100, total=700, splits=(131, 400),
+                               options=opts(prefill_split_chunks=split), idx_dtype=torch.int64)
+    print(f"H={H} Hqk={Hqk} split {split}: worst state rel {err:.2e}")
+
+
+def test_bf16_pool_gqa_head_placement():
+    pre, pool = make_case([0, 37, 1000], [500, 190, 300], ps=128, H=32, Hqk=16, seed=77,
+                          g_scale=0.3)
+    pool = pool.to(torch.bfloat16)
+    _, writes, err = check_paged_prefill(pre, pool)
+    print(f"bf16 pool, H=32 Hqk=16: worst state rel {err:.2e}")
 
 
 # ---- bf16 state pools: states stored rounded to bf16, arithmetic in fp32
 
-@pytest.mark.parametrize("split", [None, "2"])
+@pytest.mark.parametrize("split", [-1, 2])
 def test_bf16_pool_prefill(split):
     """Paged prefill on a bf16 pool (whole sequences, and forced segments of
     2 chunks): bf16 read rows, rounded page-boundary and final stores, the
     write set and every untouched row bit for bit."""
-    if split:
-        os.environ["GDN_PREFILL_SPLIT_CHUNKS"] = split
-    try:
-        pre, pool = make_case([0, 37, 128, 1000], [700, 1, 64, 900], ps=128, H=4, Hqk=2,
-                              seed=31, g_scale=0.3)
-        pool = pool.to(torch.bfloat16)
-        _, writes, err = check_paged_prefill(pre, pool)
-        assert len(writes) > 4
-        print(f"bf16 pool prefill (split {split}): worst state rel {err:.2e}")
-    finally:
-        os.environ.pop("GDN_PREFILL_SPLIT_CHUNKS", None)
+    pre, pool = make_case([0, 37, 128, 1000], [700, 1, 64, 900], ps=128, H=4, Hqk=2,
+                          seed=31, g_scale=0.3)
+    pool = pool.to(torch.bfloat16)
+    _, writes, err = check_paged_prefill(pre, pool, options=opts(prefill_split_chunks=split))
+    assert len(writes) > 4
+    print(f"bf16 pool prefill (split {split}): worst state rel {err:.2e}")
 
 
 def test_bf16_pool_prefill_then_decode():
@@ -547,40 +581,8 @@ def test_bf16_pool_decode_batch():
 def test_bf16_general_prefill_checkpoints():
     """Slot-argument prefill in pieces on bf16 state buffers with checkpoints
     every 100 tokens (inside chunks) into a separate bf16 buffer."""
-    m = lib()
-    H = 2
-    N = 100
-    c = cuda(workloads.config3(heads=H, total=1000, splits=(131, 400, 640), every_n=N,
-                               num_rows=3, g_scale=0.1))
-    slot_pool = c["pool"].to(torch.bfloat16)
-    ckpt = workloads.nan_pool(1000 // N, H, 128, 128, device=DEV).to(torch.bfloat16)
-    ref_slot = np.zeros((3, H, 128, 128))
-    ref_ck = {}
-    for call in c["calls"]:
-        o = m.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"], call["cu_seqlens"],
-                      initial_state=slot_pool, state_indices=call["state_indices"],
-                      output_state=slot_pool, output_state_indices=call["output_state_indices"],
-                      output_final_state=True, state_checkpoints=ckpt,
-                      checkpoint_state_indices=c["checkpoint_state_indices"],
-                      checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                      prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=N)
-        torch.cuda.synchronize()
-        res = ogdn.prefill(call["q"].cpu(), call["k"].cpu(), call["v"].cpu(), call["g"].cpu(),
-                           call["beta"].cpu(), call["cu_seqlens"].cpu(), initial_state=ref_slot,
-                           state_indices=call["state_indices"].tolist(), output_final_state=True,
-                           output_state_indices=call["output_state_indices"].tolist(),
-                           checkpoint_state_indices=c["checkpoint_state_indices"].tolist(),
-                           checkpoint_cu_starts=call["checkpoint_cu_starts"].tolist(),
-                           prefix_lens=call["prefix_lens"].tolist(), checkpoint_every_n_tokens=N,
-                           shared_pool=False, state_dtype="bf16")
-        check_outputs(o, res.o)
-        ref_slot = ogdn.apply_writes(ref_slot, res.final)
-        ref_ck.update(res.checkpoints)
-        check_state(slot_pool[c["slot"]], ref_slot[c["slot"]], "slot")
-    got = [r for r in range(1000 // N) if torch.isfinite(ckpt[r].float()).all()]
-    assert got == sorted(ref_ck)
-    for r, st in ref_ck.items():
-        check_state(ckpt[r], st, f"checkpoint {r}")
+    err = check_sliced_general(H=2, N=100, state_dtype=torch.bfloat16)
+    print(f"bf16 general: worst state rel {err:.2e}")
 
 
 def test_state_buffers_share_one_dtype():

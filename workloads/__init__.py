@@ -216,17 +216,19 @@ def config2(device="cpu", seed: int = 2, num_seqs: int = 256, qk_heads: int = 16
 
 def config3(device="cpu", seed: int = 3, heads: int = 32, total: int = 32768,
             splits=(7001, 14500, 20000, 27777), every_n: int = 896,
-            num_rows: int = 64, g_scale: float = 1.0) -> Dict:
+            num_rows: int = 64, g_scale: float = 1.0, qk_heads: Optional[int] = None) -> Dict:
     """Long chunked prefill with checkpoints, B = 1, fed in len(splits)+1 calls.
 
     Each call uses the slot-argument form: the request's state lives in slot
     row ``slot`` of a ``num_rows``-row pool (read -1 on the first call, then the
     slot), and checkpoints every ``every_n`` tokens go to a separate NaN-filled
     ``state_checkpoints`` buffer; checkpoint c (position (c+1)*every_n) is
-    stored at row c for even c and skipped (-1) for odd c.
+    stored at row c for even c and skipped (-1) for odd c.  ``qk_heads``
+    (default ``heads``) q/k heads serve the ``heads`` v-heads.
     """
     gen = generator(seed)
-    H = Hqk = heads
+    H = heads
+    Hqk = qk_heads or heads
     K = V = 128
     n_ck = total // every_n
     ck_rows = torch.tensor([c if c % 2 == 0 else -1 for c in range(n_ck)], dtype=torch.int32)
@@ -253,7 +255,8 @@ def config4(device="cpu", seed: int = 4, heads: int = 32, num_prefill: int = 32,
             prefill_pad: int = 4, num_decode: int = 512, decode_pad: int = 16,
             page_size: int = 896, num_pages: int = 16384, new_lo: int = 512,
             new_hi: int = 8192, hit_hi: int = 16384, ctx_lo: int = 2048,
-            ctx_hi: int = 65536, layers: Sequence[int] = (0,), g_scale: float = 1.0) -> Dict:
+            ctx_hi: int = 65536, layers: Sequence[int] = (0,), g_scale: float = 1.0,
+            qk_heads: Optional[int] = None) -> Dict:
     """Mixed hybrid serving step on one pool.
 
     Prefill: ``num_prefill`` sequences, new tokens ~ U[new_lo, new_hi], prefix
@@ -264,10 +267,12 @@ def config4(device="cpu", seed: int = 4, heads: int = 32, num_prefill: int = 32,
     or writes has its own id; page-list entries before the read page (cold
     prefix pages nobody touches) are drawn from a shared cold region.  The page
     tables are drawn once; token inputs are drawn per layer from seed
-    ``seed * 1000 + layer``.
+    ``seed * 1000 + layer``.  ``qk_heads`` (default ``heads``) q/k heads serve
+    the ``heads`` v-heads.
     """
     gen = generator(seed)
-    H = Hqk = heads
+    H = heads
+    Hqk = qk_heads or heads
     K = V = 128
     perm = _perm(num_pages, gen)
     hot = iter(perm)
