@@ -220,6 +220,31 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gdn_prefill_paged_noalloc -- gdn_prefill_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments and results, without
+ * the workspace.  Its workspace is a fixed scratch array of 256 MiB that the
+ * library holds on every device it runs on, from its load until the process
+ * ends; the call allocates nothing (its first call on a device only looks up
+ * that array's address).  Every call on one device shares that device's
+ * scratch and leaves its contents behind (nothing in it needs to start at
+ * zero): calls that overlap on one device -- on two streams, or from two
+ * threads -- race and give undefined results.  A call whose workspace
+ * for its own T and B would exceed 256 MiB fails with GDN_EWORKSPACE before
+ * any launch: at 32 v-heads, beyond about 28k new tokens in one sequence,
+ * 19k in 8 sequences (batches that may run sequence-parallel also hold
+ * segment states) and 43k in 36 sequences.
+ * Errors: as gdn_prefill_paged.
+ */
+int gdn_prefill_paged_noalloc(const gdn_dims_t* dims, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              void* state_pool, int64_t pool_row_stride,
+                              const int32_t* page_indices, const int32_t* page_indptr,
+                              const int32_t* last_page_len, int32_t page_size,
+                              const gdn_prefill_slots_t* slots, void* o, hipStream_t stream);
+
+/*
  * gdn_decode_paged -- one token per sequence on a paged pool (flashinfer.gdn_paged,
  * gated_delta_rule_decode_paged): last_page_len[b] == 1 reads page n-2 and
  * writes page n-1, otherwise the last page is updated in place.  Every

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     lib_path,
     prefill,
     prefill_paged,
+    prefill_paged_noalloc,
     prefill_slots,
     prefill_workspace_size,
     version,

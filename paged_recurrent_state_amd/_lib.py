@@ -77,7 +77,7 @@ class DecodeSlots(NamedTuple):
 
 
 EXPORTS = ["gdn_prefill_slots", "gdn_decode_slots", "gdn_prefill_workspace_size",
-           "gdn_prefill_paged", "gdn_decode_paged", "gdn_prefill", "gdn_decode",
+           "gdn_prefill_paged", "gdn_prefill_paged_noalloc", "gdn_decode_paged", "gdn_prefill", "gdn_decode",
            "gdn_block_table_to_csr", "gdn_csr_to_block_table", "gdn_last_error", "gdn_version"]
 
 
@@ -100,6 +100,9 @@ def load():
         "gdn_prefill_workspace_size": (SZ, [I64, I32, C.POINTER(Dims)]),
         "gdn_prefill_paged": (C.c_int, [C.POINTER(Dims), P, P, P, P, P, P, I32, I64, P, I64,
                                         P, P, P, I32, C.POINTER(_PrefillSlotsC), P, P, SZ, P]),
+        "gdn_prefill_paged_noalloc": (C.c_int, [C.POINTER(Dims), P, P, P, P, P, P, I32, I64, P,
+                                                I64, P, P, P, I32, C.POINTER(_PrefillSlotsC),
+                                                P, P]),
         "gdn_decode_paged": (C.c_int, [C.POINTER(Dims), P, P, P, P, P, I32, P, I64, P, P, P,
                                        I32, C.POINTER(_DecodeSlotsC), P, P]),
         "gdn_prefill": (C.c_int, [C.POINTER(Dims), P, P, P, P, P, P, I32, I64, P, I64, P, P,
@@ -348,6 +351,38 @@ def prefill_paged(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_i
                                  _ptr(page_indices), _ptr(page_indptr), _ptr(last_page_len),
                                  int(page_size), sc, _ptr(o), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev)))
+    return o
+
+
+def prefill_paged_noalloc(q, k, v, g, beta, cu_seqlens, state_pool, page_indices, page_indptr,
+                          page_size: int, last_page_len, slots: Optional[PrefillSlots] = None,
+                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                          options: Optional[Options] = None) -> torch.Tensor:
+    """prefill_paged with the library's fixed per-device scratch as its workspace (no
+    device allocation by the library; pass ``out`` for none at all).  Calls that
+    overlap on one device race on that scratch."""
+    lib = load()
+    dev = q.device
+    T = q.shape[0]
+    _token_checks(q, k, v, g, beta, dev, T)
+    for t, nm in ((cu_seqlens, "cu_seqlens"), (page_indices, "page_indices"),
+                  (page_indptr, "page_indptr"), (last_page_len, "last_page_len")):
+        _need(t, nm, torch.int32, dev)
+    d = _dims(q, v, scale, _state_dtype(dev, (state_pool, "state_pool")), options)
+    stride = _pool_stride(state_pool, "state_pool", d.num_v_heads, d.head_dim_v, d.head_dim_k)
+    B = last_page_len.shape[0]
+    o = out if out is not None else torch.empty(T, d.num_v_heads, d.head_dim_v,
+                                                dtype=torch.bfloat16, device=dev)
+    sc = None
+    if slots is not None:
+        for t, nm in zip(slots, PrefillSlots._fields):
+            _need(t, nm, torch.int32, dev)
+        sc = C.byref(_PrefillSlotsC(*[t.data_ptr() for t in slots]))
+    _check(lib.gdn_prefill_paged_noalloc(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _ptr(beta), _ptr(cu_seqlens), B, T, _ptr(state_pool),
+                                         stride, _ptr(page_indices), _ptr(page_indptr),
+                                         _ptr(last_page_len), int(page_size), sc, _ptr(o),
+                                         _stream(dev)))
     return o
 
 

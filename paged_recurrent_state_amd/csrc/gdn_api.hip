@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gdn_internal.h"
@@ -261,6 +262,91 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   return ok();
 }
 
+// Scratch of gdn_prefill_paged_noalloc: the workspace of calls that may not
+// allocate, one copy per device, held from the library's load until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ELAUNCH, "no current HIP device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(GDN_ELAUNCH, "device address of the fixed scratch: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
+// The paged prefill; with `fixed_scratch` its workspace is the device's
+// fixed scratch instead of the caller's.
+int prefill_paged_impl(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const int32_t* cu_seqlens,
+                       int32_t num_seqs, int64_t total_tokens, void* state_pool,
+                       int64_t pool_row_stride, const int32_t* page_indices,
+                       const int32_t* page_indptr, const int32_t* last_page_len,
+                       int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
+                       void* workspace, size_t workspace_bytes, bool fixed_scratch,
+                       hipStream_t stream) {
+  if (int rc = check_dims(dims)) return rc;
+  if (num_seqs < 0 || total_tokens < 0)
+    return fail(GDN_EINVAL, "num_seqs and total_tokens must be >= 0");
+  if (int rc = check_page_size(page_size)) return rc;
+  if (!cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must not be NULL");
+  if (!state_pool) return fail(GDN_EINVAL, "state_pool must not be NULL");
+  if (!page_indices || !page_indptr || !last_page_len)
+    return fail(GDN_EINVAL, "page table must not be NULL");
+  if (pool_row_stride < state_block(dims))
+    return fail(GDN_EINVAL, "pool_row_stride %lld < H*V*K", (long long)pool_row_stride);
+  if (num_seqs == 0) return ok();
+  if (total_tokens > 0)
+    if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
+  if (slots && (!slots->state_indices || !slots->output_state_indices ||
+                !slots->checkpoint_cu_starts || !slots->prefix_lens || !slots->chunk_starts))
+    return fail(GDN_EINVAL, "every slot array must be given");
+  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, get_opts(dims).split);
+  if (fixed_scratch) {
+    if (L.total > kScratchBytes)
+      return fail(GDN_EWORKSPACE,
+                  "this call needs %zu bytes of workspace; the fixed scratch holds %zu "
+                  "(use gdn_prefill_paged with a workspace)", L.total, kScratchBytes);
+    if (int rc = scratch_for_current_device(&workspace)) return rc;
+    workspace_bytes = kScratchBytes;
+  }
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
+    return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
+                workspace_bytes);
+  SlotsDev sd;
+  if (slots) {
+    sd = SlotsDev{slots->state_indices, slots->output_state_indices, slots->checkpoint_cu_starts,
+                  slots->prefix_lens, slots->chunk_starts};
+  } else {
+    sd = carve_slots(workspace, L, num_seqs);
+    if (int rc = launched(launch_prefill_slots(cu_seqlens, page_indices, page_indptr,
+                                               last_page_len, num_seqs, page_size,
+                                               (int32_t*)sd.read, (int32_t*)sd.write,
+                                               (int32_t*)sd.ckpt_start, (int32_t*)sd.prefix,
+                                               (int32_t*)sd.chunk_start, stream),
+                          "prefill slot kernel"))
+      return rc;
+  }
+  if (total_tokens == 0) return ok();
+  // The paged call is the slot-argument call with one pool for all three
+  // buffers and a checkpoint every page_size tokens into page_indices.
+  return run_prefill(dims, q, k, v, g, beta, cu_seqlens, num_seqs, sd, L, workspace, state_pool,
+                     pool_row_stride, state_pool, pool_row_stride, state_pool, pool_row_stride,
+                     page_indices, 0, page_size, o, stream);
+}
+
 }  // namespace
 
 namespace gdn {
@@ -377,46 +463,22 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
                       const int32_t* page_indptr, const int32_t* last_page_len,
                       int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (int rc = check_dims(dims)) return rc;
-  if (num_seqs < 0 || total_tokens < 0)
-    return fail(GDN_EINVAL, "num_seqs and total_tokens must be >= 0");
-  if (int rc = check_page_size(page_size)) return rc;
-  if (!cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must not be NULL");
-  if (!state_pool) return fail(GDN_EINVAL, "state_pool must not be NULL");
-  if (!page_indices || !page_indptr || !last_page_len)
-    return fail(GDN_EINVAL, "page table must not be NULL");
-  if (pool_row_stride < state_block(dims))
-    return fail(GDN_EINVAL, "pool_row_stride %lld < H*V*K", (long long)pool_row_stride);
-  if (num_seqs == 0) return ok();
-  if (total_tokens > 0)
-    if (int rc = check_tokens(q, k, v, cu_seqlens, o)) return rc;
-  const WsLayout L = ws_layout(total_tokens, num_seqs, dims->num_v_heads, get_opts(dims).split);
-  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
-    return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
-                workspace_bytes);
-  SlotsDev sd;
-  if (slots) {
-    if (!slots->state_indices || !slots->output_state_indices || !slots->checkpoint_cu_starts ||
-        !slots->prefix_lens || !slots->chunk_starts)
-      return fail(GDN_EINVAL, "every slot array must be given");
-    sd = SlotsDev{slots->state_indices, slots->output_state_indices, slots->checkpoint_cu_starts,
-                  slots->prefix_lens, slots->chunk_starts};
-  } else {
-    sd = carve_slots(workspace, L, num_seqs);
-    if (int rc = launched(launch_prefill_slots(cu_seqlens, page_indices, page_indptr,
-                                               last_page_len, num_seqs, page_size,
-                                               (int32_t*)sd.read, (int32_t*)sd.write,
-                                               (int32_t*)sd.ckpt_start, (int32_t*)sd.prefix,
-                                               (int32_t*)sd.chunk_start, stream),
-                          "prefill slot kernel"))
-      return rc;
-  }
-  if (total_tokens == 0) return ok();
-  // The paged call is the slot-argument call with one pool for all three
-  // buffers and a checkpoint every page_size tokens into page_indices.
-  return run_prefill(dims, q, k, v, g, beta, cu_seqlens, num_seqs, sd, L, workspace, state_pool,
-                     pool_row_stride, state_pool, pool_row_stride, state_pool, pool_row_stride,
-                     page_indices, 0, page_size, o, stream);
+  return prefill_paged_impl(dims, q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                            state_pool, pool_row_stride, page_indices, page_indptr,
+                            last_page_len, page_size, slots, o, workspace, workspace_bytes,
+                            false, stream);
+}
+
+int gdn_prefill_paged_noalloc(const gdn_dims_t* dims, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              void* state_pool, int64_t pool_row_stride,
+                              const int32_t* page_indices, const int32_t* page_indptr,
+                              const int32_t* last_page_len, int32_t page_size,
+                              const gdn_prefill_slots_t* slots, void* o, hipStream_t stream) {
+  return prefill_paged_impl(dims, q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                            state_pool, pool_row_stride, page_indices, page_indptr,
+                            last_page_len, page_size, slots, o, nullptr, 0, true, stream);
 }
 
 int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
