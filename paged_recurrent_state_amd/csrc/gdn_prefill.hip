@@ -1126,9 +1126,10 @@ __device__ void plan_body(const int32_t* __restrict__ cu, const int32_t* __restr
   }
 }
 
-// Sequence-parallel plan, one workgroup.  Sequence b (G = ceil(chunks / m)
-// segments of m chunks; segment g starts at new token lo_g, an absolute
-// multiple of 64 for g >= 1) gets, when G >= 2:
+// Sequence-parallel plan, one workgroup.  Sequence b is cut into G segments
+// of s chunks (the last one shorter): s = m when m is forced, the balanced
+// length ceil(c / ceil(c / m)) under the auto plan; segment g starts at new
+// token lo_g, an absolute multiple of 64 for g >= 1.  It gets, when G >= 2:
 //   first pass:  for g = 0 .. G-2 the segment from the zero state (its offset
 //                N_g) and from the identity with v = 0 (its transition M_g),
 //                so that S_end = S_start M_g + N_g;
@@ -1147,22 +1148,26 @@ __device__ void plan_body(const int32_t* __restrict__ cu, const int32_t* __restr
 // second pass from its own read row, in one workgroup per (sequence, head,
 // V-tile) that reads before it writes.
 
-// Auto plan: the cost, in chunks of the whole-sequence recurrence on one
-// compute unit, of running the batch whole and cut into segments of m
-// chunks, and the m (or none) that costs least.  Items are (sequence, head)
-// runs, P of them resident at once (one recurrence workgroup per compute
-// unit); a pass of items of at most m chunks takes about m per round of P.
-//   whole:  max(c_max, H sum(c) / P)
-//   split:  first pass  a1 m ceil(2 H sum(G - 1) / P)
-//           scan        a_s (G_max - 1) ceil(8 B H / CUs)   (8 workgroups a pair)
-//           second pass max(m, H sum(c) / P)
-//           + launches  a_l
-// with a1 the relative cost of a first-pass chunk (no outputs) and a_s of
-// one composition step of the scan.
-constexpr float kCostPass1 = 0.8f;
-constexpr float kCostScanStep = 0.5f;
+// Auto plan: the segment length m (or none) that minimises an estimate of
+// the recurrence's time, in chunk-steps of one recurrence workgroup.  A
+// sequence of c chunks is cut into G = ceil(c / s) segments of s =
+// ceil(c / ceil(c / m)) chunks (balanced: no short tail segment).  Each pass
+// is a list of (sequence, head) runs dealt longest first to the P that are
+// resident at once (one recurrence workgroup per compute unit); for N runs
+// of total length W and longest p its time is taken as p when N <= P, else
+// max(p, W / P + W / N) (the longest-first bound W / P + p_(P+1) with the
+// mean length standing in for the (P+1)-th longest).  Per plan:
+//   whole sequences:  runs(c, H each)
+//   cut:  a1 * first pass (2 (G - 1) H runs of s)
+//       + a_s * scan ((G_max - 1) steps, 8 workgroups a pair, in rounds of the CUs)
+//       + second pass (G H runs of at most s) + a_l (the two extra launches)
+// a1 = 1.0, a_s = 0.75 and a_l = 2 fit the measured times of the 8-sequence
+// 16-head ragged batch and the 32-head single prompt over segment lengths
+// 6 .. 32 (a first-pass chunk, without outputs, takes about as long as a
+// full one: the chunk's dependency chain, not its output work, sets it).
+constexpr float kCostPass1 = 1.0f;
+constexpr float kCostScanStep = 0.75f;
 constexpr float kCostLaunches = 2.0f;
-constexpr int kAutoMaxSegs = 65;  // candidates: the longest sequence in 2 .. 65 segments
 
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -1174,64 +1179,114 @@ __device__ __forceinline__ int wave_max(int x) {
   for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
   return x;
 }
+__device__ __forceinline__ float wave_sumf(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// time of N runs of total length W, the longest p, P resident at once
+__device__ __forceinline__ float pass_time(float N, float W, float pmax, float P) {
+  if (N <= P) return pmax;
+  return fmaxf(pmax, W / P + W / N);
+}
+
+// segment length (chunks) of a sequence of c chunks under the auto plan's m
+__device__ __forceinline__ int balanced_len(int c, int m) {
+  const int G = (c + m - 1) / m;
+  return (c + G - 1) / G;
+}
 
 // Segment length of the auto plan (0: whole sequences), the same in every
 // thread.  B <= 256 (the host enables the auto plan only when B H <= 256).
+// Lane j of every wave evaluates candidate j (the longest sequence in j + 2
+// segments) over the wave's share of the sequences; the shares meet once in
+// LDS, where wave 0 prices the 64 candidates and picks the cheapest.
+constexpr int kAutoWaves = 4;
 __device__ int auto_split_m(const PrefillParams& p) {
   __shared__ int cnt[256];
-  if (p.num_seqs > 256) return 0;
-  __shared__ float wcost[kPlanTile / 64];
-  __shared__ int wm[kPlanTile / 64];
+  __shared__ int part_i[kAutoWaves][6][64];
+  __shared__ float part_f[kAutoWaves][64];
+  __shared__ int chosen;
   const int B = p.num_seqs, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nw = blockDim.x >> 6;
+  if (B > 256) return 0;
   if (tid < B) cnt[tid] = chunks_of(p.slots.prefix[tid], p.cu_seqlens[tid + 1] - p.cu_seqlens[tid]);
   __syncthreads();
-  int cmax = 0, csum = 0;
-  for (int i = lane; i < B; i += 64) {
-    cmax = max(cmax, cnt[i]);
-    csum += cnt[i];
-  }
-  cmax = wave_max(cmax);
-  csum = wave_sum(csum);
-  const float P = fmaxf(1.f, (float)(p.num_cus * p.tile_waves / 8));
-  const float H = (float)p.H;
-  const float rounds_scan = ceilf(8.f * B * p.H / fmaxf(1.f, (float)p.num_cus));
-  float best = fmaxf((float)cmax, H * csum / P);
-  int best_m = 0;
-  for (int G = 2 + wid; G <= kAutoMaxSegs; G += nw) {
-    const int m = max(kSplitMinChunks, (cmax + G - 1) / G);
-    if (m >= cmax) continue;  // nothing would be cut
-    int sg = 0, sg1 = 0, gmax = 0;
-    for (int i = lane; i < B; i += 64) {
-      const int g = (cnt[i] + m - 1) / m;
+  if (wid < kAutoWaves) {
+    int cmax = 0;
+    for (int i = lane; i < B; i += 64) cmax = max(cmax, cnt[i]);
+    cmax = wave_max(cmax);
+    const int m = max(kSplitMinChunks, (cmax + lane + 1) / (lane + 2));  // candidate lane: lane + 2 segments
+    int sg = 0, sg1 = 0, gmax = 0, p1 = 0, p2 = 0;
+    float w1 = 0.f;
+    for (int i = wid; i < B; i += kAutoWaves) {
+      const int c = cnt[i];  // the same address in every lane: one broadcast read
+      if (c <= 0) continue;
+      const int sl = balanced_len(c, m);
+      const int g = (c + sl - 1) / sl;
       sg += g;
-      sg1 += max(g - 1, 0);
+      sg1 += g - 1;
       gmax = max(gmax, g);
+      p2 = max(p2, sl);
+      if (g > 1) {
+        p1 = max(p1, sl);
+        w1 += (float)((g - 1) * sl);
+      }
     }
-    sg = wave_sum(sg);
-    sg1 = wave_sum(sg1);
-    gmax = wave_max(gmax);
-    if (sg > p.seg_cap2 || 2 * sg1 > p.seg_cap1) continue;  // beyond the workspace's room
-    const float cost = kCostPass1 * m * ceilf(2.f * H * sg1 / P) + kCostScanStep * (gmax - 1) * rounds_scan +
-                       fmaxf((float)m, H * csum / P) + kCostLaunches;
-    if (cost < best) {
-      best = cost;
-      best_m = m;
-    }
-  }
-  if (lane == 0) {
-    wcost[wid] = best;
-    wm[wid] = best_m;
+    part_i[wid][0][lane] = sg;
+    part_i[wid][1][lane] = sg1;
+    part_i[wid][2][lane] = gmax;
+    part_i[wid][3][lane] = p1;
+    part_i[wid][4][lane] = p2;
+    part_i[wid][5][lane] = cmax;
+    part_f[wid][lane] = w1;
   }
   __syncthreads();
-  float b = wcost[0];
-  int bm = wm[0];
-  for (int w = 1; w < nw; ++w)
-    if (wcost[w] < b || (wcost[w] == b && wm[w] > bm)) {
-      b = wcost[w];
-      bm = wm[w];
+  if (wid == 0) {
+    int sg = 0, sg1 = 0, gmax = 0, p1 = 0, p2 = 0, csum = 0, nact = 0;
+    float w1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAutoWaves; ++w) {
+      sg += part_i[w][0][lane];
+      sg1 += part_i[w][1][lane];
+      gmax = max(gmax, part_i[w][2][lane]);
+      p1 = max(p1, part_i[w][3][lane]);
+      p2 = max(p2, part_i[w][4][lane]);
+      w1 += part_f[w][lane];
     }
-  return bm;
+    const int cmax = part_i[0][5][lane];
+    for (int i = lane; i < B; i += 64) {
+      csum += cnt[i];
+      nact += cnt[i] > 0;
+    }
+    csum = wave_sum(csum);
+    nact = wave_sum(nact);
+    const int m = max(kSplitMinChunks, (cmax + lane + 1) / (lane + 2));
+    const float P = fmaxf(1.f, (float)(p.num_cus * p.tile_waves / 8));
+    const float H = (float)p.H;
+    const float rounds_scan = ceilf(8.f * B * p.H / fmaxf(1.f, (float)p.num_cus));
+    const float whole = pass_time(H * nact, H * csum, (float)cmax, P);
+    float cost = whole;
+    if (m < cmax && sg <= p.seg_cap2 && 2 * sg1 <= p.seg_cap1)
+      cost = kCostPass1 * pass_time(2.f * H * sg1, 2.f * H * w1, (float)p1, P) +
+             kCostScanStep * (gmax - 1) * rounds_scan + pass_time(H * sg, H * csum, (float)p2, P) +
+             kCostLaunches;
+    // cheapest candidate (ties: the longer segments), whole sequences unless one beats them
+    float best = cost < whole ? cost : whole;
+    int bm = cost < whole ? m : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ob = __shfl_xor(best, off, 64);
+      const int om = __shfl_xor(bm, off, 64);
+      if (ob < best || (ob == best && om > bm)) {
+        best = ob;
+        bm = om;
+      }
+    }
+    if (lane == 0) chosen = bm;
+  }
+  __syncthreads();
+  return chosen;
 }
 
 __device__ void split_plan(const PrefillParams& p) {
@@ -1240,12 +1295,13 @@ __device__ void split_plan(const PrefillParams& p) {
   int carry1 = 0, carry2 = 0, carry_row = 0;
   for (int base = 0; base < B; base += blockDim.x) {
     const int b = base + (int)threadIdx.x;
-    int L = 0, pre = 0, G = 0;
+    int L = 0, pre = 0, G = 0, mm = 1;  // mm: this sequence's segment length (chunks)
     if (b < B) {
       L = p.cu_seqlens[b + 1] - p.cu_seqlens[b];
       pre = p.slots.prefix[b];
       const int c = chunks_of(pre, L);
-      G = L <= 0 ? 0 : m > 0 ? (c + m - 1) / m : 1;
+      if (m > 0 && c > 0) mm = p.split_mode == kSplitAuto ? balanced_len(c, m) : m;
+      G = L <= 0 ? 0 : m > 0 ? (c + mm - 1) / mm : 1;
     }
     const int n1 = G > 1 ? 2 * (G - 1) : 0, n2 = G, nrow = G > 1 ? 3 * G - 2 : 0;
     int t1, t2, trow;
@@ -1258,7 +1314,6 @@ __device__ void split_plan(const PrefillParams& p) {
       const int rd = p.slots.read[b], wr = p.slots.write[b];
       const int ckb = p.ckpt_idx ? p.slots.ckpt_start[b] : 0;
       const int nbase = (pre & ~(kChunk - 1)) - pre;
-      const int mm = max(m, 1);
       auto lo = [&](int g) { return g == 0 ? 0 : nbase + kChunk * mm * g; };
       auto hi = [&](int g) { return G == 1 ? L : min(L, nbase + kChunk * mm * (g + 1)); };
       auto put = [](int32_t* d, int a, int b_, int c, int e, int f, int g_, int h, int i) {

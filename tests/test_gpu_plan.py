@@ -95,6 +95,9 @@ def test_plan_records(split):
         for x, y in zip(mine2, mine2[1:]):
             assert y[0] == x[0] + x[1]
         assert [int(r[5]) for r in mine2] == [-1] * (G - 1) + [wr[b]]
+        if split == 0 and G > 1:  # balanced: interior segments share one length
+            lens = [int(r[1]) for r in mine2[1:-1]]
+            assert len(set(lens)) <= 1
         if G == 1:
             assert mine2[0][4] == rd[b]  # a whole sequence reads its own row
             continue
