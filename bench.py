@@ -50,9 +50,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side", action="store_true",
-                    help="skip the side measurements (bf16-pool decode, long single prompt)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    ap.add_argument("--cpu-sample-decode", type=int, default=128)
+                    help="skip the other workloads (paged prefill, paged decode, long prompt)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (reference for "
                          "hardware byte counters); reported as copy_GBps")
@@ -111,48 +109,126 @@ def decode_bytes(B: int, H: int, Hqk: int) -> int:
 
 
 # ----------------------------------------------------------------- CPU baseline
-def cpu_baseline(pre_cpu, dec_cpu, pool_rows, sample_tokens, sample_decode, layers,
-                 step_prefill_tokens, step_decode_seqs):
-    """Time the fp64 oracle on a bounded sample of layer 0 and scale to the step."""
-    import numpy as np
+# The fp64 oracle timed on the host cores: worker processes (started fresh,
+# one oracle thread each) draw seeded inputs of a workload's shapes and
+# distributions on the CPU and time only the oracle call on them.  The
+# measured per-token (prefill) and per-sequence (decode) times then give each
+# workload's time: its sequences dealt longest first to the cores (heads split
+# over the cores when one sequence is all there is).
+
+def cpu_cores() -> int:
+    """Host cores this process may use, capped at the 16 a one-GPU share has."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_item(item):
+    """One timed oracle run (worker process): item = (kind, n, Hqk, H, seed)."""
+    import torch
     from threadpoolctl import threadpool_limits
 
+    import workloads
     from oracle import gdn as ogdn
-
-    class Rows:
-        def __getitem__(self, r):
-            return pool_rows[int(r)]
-
+    kind, n, Hqk, H, seed = item
     with threadpool_limits(limits=1):
-        # prefill sample: the first `sample_tokens` new tokens of sequence 0
-        L0 = int(pre_cpu["new"][0])
-        n = min(sample_tokens, L0)
-        q, k, v = pre_cpu["q"][:n], pre_cpu["k"][:n], pre_cpu["v"][:n]
-        g, beta = pre_cpu["g"][:n], pre_cpu["beta"][:n]
-        rd = pre_cpu["read_rows"][0]
+        torch.set_num_threads(1)
+        gen = workloads.generator(seed)
+        t = workloads.token_inputs(n, Hqk, H, D, D, gen)
+        s0 = (torch.randn(1, H, D, D, generator=gen, dtype=torch.float64) / math.sqrt(D)).numpy()
         t0 = time.perf_counter()
-        ogdn.prefill(q, k, v, g, beta, [0, n], initial_state=Rows(),
-                     state_indices=[rd], output_final_state=True, output_state_indices=[rd])
-        t_pf = (time.perf_counter() - t0) / n
-        # decode sample: the first `sample_decode` sequences
-        m = sample_decode
-        rows = dec_cpu["read_rows"][:m]
-        t0 = time.perf_counter()
-        ogdn.decode(dec_cpu["q"][:m], dec_cpu["k"][:m], dec_cpu["v"][:m], dec_cpu["g"][:m],
-                    dec_cpu["beta"][:m], initial_state=Rows(), initial_state_indices=rows)
-        t_dec = (time.perf_counter() - t0) / m
-    step_s = layers * (t_pf * step_prefill_tokens + t_dec * step_decode_seqs)
+        if kind == "prefill":
+            ogdn.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], [0, n], initial_state=s0,
+                         state_indices=[0], output_final_state=True, shared_pool=False)
+        else:  # n sequences of one decode token each
+            ogdn.decode(t["q"], t["k"], t["v"], t["g"], t["beta"], initial_state=s0,
+                        initial_state_indices=[0] * n, output_state_indices=[-1] * n,
+                        shared_pool=False)
+        dt = time.perf_counter() - t0
+    return os.getpid(), dt
+
+
+def _lpt(times, cores):
+    loads = [0.0] * cores
+    for x in sorted(times, reverse=True):
+        i = loads.index(min(loads))
+        loads[i] += x
+    return max(loads)
+
+
+def cpu_baseline(shapes, layers, n_tok=768, n_dec=96):
+    """Oracle rates on the host cores (multi-core and 1 core).
+
+    shapes: per workload, dict(prefill=[new tokens per sequence], H, Hqk,
+    decode=number of decode sequences, Hd, Hqkd).  Per (H, Hqk) head layout,
+    `cores` workers each time n_tok prefill tokens and n_dec decode sequences
+    at once (contended, as the multi-core run would be), and one worker alone
+    (the 1-core rate)."""
+    import multiprocessing as mp
+    C = cpu_cores()
+    layouts = sorted({(w["H"], w["Hqk"]) for w in shapes.values() if w.get("prefill")} |
+                     {(w["H"] // max(1, C), w["Hqk"] // max(1, C)) for w in shapes.values()
+                      if w.get("split_heads")} |
+                     {(w["Hd"], w["Hqkd"]) for w in shapes.values() if w.get("decode")})
+    layouts = sorted({(max(1, h), max(1, q)) for h, q in layouts})
+    per_tok, per_dec = {}, {}
+    ctx = mp.get_context("spawn")
+    t_start = time.perf_counter()
+    with ctx.Pool(C) as pool:
+        # start every worker and run each code path once before timing
+        pool.map(_oracle_item, [("prefill", 8, 2, 2, 0)] * C + [("decode", 4, 2, 2, 0)] * C,
+                 chunksize=1)
+        for (H, Hqk) in layouts:
+            for kind, n in (("prefill", n_tok), ("decode", n_dec)):
+                items = [(kind, n, Hqk, H, 1000 + i) for i in range(C)]
+                res = pool.map(_oracle_item, items, chunksize=1)
+                multi = max(dt for _, dt in res) / n  # contended, per unit
+                single = _oracle_item((kind, n, Hqk, H, 7))[1] / n
+                (per_tok if kind == "prefill" else per_dec)[(H, Hqk)] = (multi, single)
+    wall = time.perf_counter() - t_start
+    out = {}
+    for name, w in shapes.items():
+        r = {}
+        if w.get("prefill"):
+            lens = [x for x in w["prefill"] if x > 0]
+            T = sum(lens)
+            if w.get("split_heads"):  # one sequence: its heads split over the cores
+                hh = (max(1, w["H"] // C), max(1, w["Hqk"] // C))
+                t_multi = T * per_tok[hh][0] * math.ceil(w["H"] / (hh[0] * C))
+            else:
+                t_multi = _lpt([x * per_tok[(w["H"], w["Hqk"])][0] for x in lens], C)
+            t_single = T * per_tok[(w["H"], w["Hqk"])][1]
+            r.update(prefill_tokens_per_s=T / t_multi, prefill_tokens_per_s_1core=T / t_single,
+                     prefill_s=t_multi)
+        if w.get("decode"):
+            Bd, Hd = w["decode"], w["Hd"]
+            m, s1 = per_dec[(Hd, w["Hqkd"])]
+            t_multi = math.ceil(Bd / C) * m
+            gb = 2 * Bd * Hd * STATE_BYTES / 1e9
+            r.update(decode_state_GBps=gb / t_multi, decode_state_GBps_1core=gb / (Bd * s1),
+                     decode_s=t_multi)
+        out[name] = r
+    hy = shapes["hybrid"]
+    step_multi = layers * (out["hybrid"]["prefill_s"] + out["hybrid"]["decode_s"])
+    T_h = sum(hy["prefill"])
+    p1 = per_tok[(hy["H"], hy["Hqk"])][1]
+    d1 = per_dec[(hy["Hd"], hy["Hqkd"])][1]
+    step_single = layers * (T_h * p1 + hy["decode"] * d1)
     return {
-        "value": step_prefill_tokens / step_s,
-        "unit": "prefill tokens/s",
-        "cores": 1,
+        "value": T_h / step_multi,
+        "unit": f"prefill tokens/s ({layers}-layer hybrid step incl. decode batch)",
+        "cores": C,
         "kind": "oracle",
-        "sample": (f"layer 0: {n} new tokens of prefill sequence 0 (all heads) and {m} decode "
-                   f"sequences, fp64 NumPy on 1 thread; per-token and per-sequence times "
-                   f"scaled to the step's {step_prefill_tokens} prefill tokens and "
-                   f"{step_decode_seqs} decode sequences x {layers} layers"),
-        "prefill_tokens_per_s_per_layer": 1.0 / t_pf,
-        "decode_state_GBps": (2 * STATE_BYTES * pre_cpu["H"]) / t_dec / 1e9,
+        "one_core_value": T_h / step_single,
+        "sample": (f"fp64 NumPy oracle, one thread per process, {C} processes at once and 1 "
+                   f"alone; per head layout each timed {n_tok} prefill tokens and {n_dec} decode "
+                   f"sequences of seeded inputs drawn like the workloads; workload times: "
+                   f"sequences dealt longest first to the cores (the 32-head single prompt: "
+                   f"heads split over the cores), hybrid step = layer 0 x {layers} "
+                   f"(extrapolated); {wall:.1f} s wall"),
+        "per_workload": out,
     }
 
 
@@ -174,53 +250,175 @@ def _median_ms(torch, run, n, reps=3):
     return sorted(res)[len(res) // 2]
 
 
-def side_measurements(torch, gdn, workloads, pool, dec, ps, H, Hqk, t_dc_ms):
-    """Timed beside the step, not part of it: the decode batch on a bf16 copy
-    of the pool (the same rows at half the bytes), and the long single prompt
-    (one sequence, 32 heads, 32768 tokens in 5 calls) with the
-    sequence-parallel recurrence against whole sequences."""
-    dev = pool.device
-    out = {}
-    Bd = int(dec["last_page_len"].shape[0])
-    o = torch.empty(Bd, H, D, dtype=torch.bfloat16, device=dev)
-    sl = gdn.decode_slots(dec["page_indices"], dec["page_indptr"], dec["last_page_len"])
-    pool16 = pool.to(torch.bfloat16)
-    ms = _median_ms(torch, lambda: gdn.decode_paged(
-        dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool16, dec["page_indices"],
-        dec["page_indptr"], ps, dec["last_page_len"], slots=sl, out=o), 20)
-    del pool16
-    by = decode_bytes(Bd, H, Hqk) - Bd * H * STATE_BYTES  # state rows at 2 bytes an element
-    out["bf16_pool_decode"] = {
-        "workload": f"the step's decode batch ({Bd} seqs, H={H}) on a bf16 copy of the pool",
-        "ms": ms, "state_GBps": by / (ms / 1e3) / 1e9,
-        "frac_hbm_peak": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "fp32_pool_ms": t_dc_ms}
-    c = workloads.config3(device=dev)
-    # one workspace for the largest call serves every call (sizes only grow)
-    t_max = max(int(call["q"].shape[0]) for call in c["calls"])
-    ws = torch.empty(gdn.prefill_workspace_size(t_max, 1, c["H"], c["Hqk"]), dtype=torch.uint8,
-                     device=dev)
+def _events_ms(torch, run, n, reps=3):
+    """Median over `reps` of the mean time of `n` back-to-back runs, HIP events
+    on torch's current stream (the one the library launches on), after 3
+    warm-up runs; also p10/p50/p90 of single runs."""
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    stream = torch.cuda.current_stream()
+    singles = []
+    for _ in range(max(10, n)):
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        singles.append((a, b))
+    torch.cuda.synchronize()
+    xs = sorted(a.elapsed_time(b) for a, b in singles)
+    pct = [xs[min(len(xs) - 1, int(q * len(xs)))] for q in (0.1, 0.5, 0.9)]
+    return _median_ms(torch, run, n, reps), pct
 
-    def run(options=None):
-        for call in c["calls"]:
-            gdn.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
-                        call["cu_seqlens"], initial_state=c["pool"],
-                        state_indices=call["state_indices"], output_state=c["pool"],
-                        output_state_indices=call["output_state_indices"],
-                        output_final_state=True, state_checkpoints=c["state_checkpoints"],
-                        checkpoint_state_indices=c["checkpoint_state_indices"],
-                        checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                        prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=c["every_n"],
-                        workspace=ws, options=options)
-    T = sum(int(call["q"].shape[0]) for call in c["calls"])
-    ms_split = _median_ms(torch, run, 5)
+
+def _state_rows_prefill(prefix, new, ps):
+    """State rows a paged prefill reads and stores: the read page when the
+    prefix is not empty, every page boundary crossed, and the final page."""
+    n = sum(1 for p, L in zip(prefix, new) if p > 0 and L > 0)
+    return n + sum(1 + (p + L) // ps - p // ps for p, L in zip(prefix, new) if L > 0)
+
+
+def measure_config1(torch, gdn, workloads):
+    """Paged prefill with shared prefixes (8 x 16 heads, page 1024), slots
+    passed (computed once, as a serving step does) and derived in the call."""
+    dev = "cuda"
+    c = workloads.config1(device=dev)
+    p = c["prefill"]
+    H, Hqk = c["H"], c["Hqk"]
+    T = int(p["q"].shape[0])
+    B = int(p["last_page_len"].shape[0])
+    ws = torch.empty(gdn.prefill_workspace_size(T, B, H, Hqk), dtype=torch.uint8, device=dev)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    sl = gdn.prefill_slots(p["cu_seqlens"], p["page_indices"], p["page_indptr"],
+                           p["last_page_len"], 1024)
+
+    def run(slots):
+        gdn.prefill_paged(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"], c["pool"],
+                          p["page_indices"], p["page_indptr"], 1024, p["last_page_len"],
+                          slots=slots, workspace=ws, out=o)
+    by = prefill_bytes(T, H, Hqk, _state_rows_prefill(p["prefix"], p["new"], 1024))
+    out = {"workload": "paged prefill, 8 sequences (prefix U[0,8192] not 64-aligned, new "
+                       "U[1,4096], half sharing prefix pages), H=Hqk=16, page 1024, 512-page "
+                       "fp32 pool", "tokens": T, "algorithmic_bytes": by}
+    for _ in range(20):  # both variants warm before either is timed
+        run(sl)
+        run(None)
+    for name, slots in (("slots_passed", sl), ("slots_derived", None)):
+        ms, pct = _events_ms(torch, lambda: run(slots), 20, reps=5)
+        out[name] = {"ms": ms, "ms_p10_p50_p90": pct, "prefill_tokens_per_s": T / (ms / 1e3),
+                     "GBps": by / (ms / 1e3) / 1e9,
+                     "frac_hbm_roofline": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}
     whole = gdn.Options(prefill_split_chunks=-1)
-    ms_whole = _median_ms(torch, lambda: run(whole), 5)
-    out["long_prompt"] = {
-        "workload": f"one sequence, H=Hqk={c['H']}, {T} tokens in {len(c['calls'])} calls, "
-                    f"checkpoints every {c['every_n']}",
-        "sequence_parallel_ms": ms_split, "prefill_tokens_per_s": T / (ms_split / 1e3),
-        "whole_sequence_ms": ms_whole, "speedup": ms_whole / ms_split}
-    return out
+    ms_whole, _ = _events_ms(torch, lambda: gdn.prefill_paged(
+        p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"], c["pool"], p["page_indices"],
+        p["page_indptr"], 1024, p["last_page_len"], slots=sl, workspace=ws, out=o,
+        options=whole), 20)
+    out["whole_sequences_ms"] = ms_whole
+    shape = dict(prefill=list(p["new"]), H=H, Hqk=Hqk)
+    del c, ws, o
+    return out, shape
+
+
+def measure_config2(torch, gdn, workloads):
+    """Paged decode (256 sequences, 16 q/k heads on 32 v-heads, page 1024),
+    four page tables with disjoint touched pages used in turn so the Infinity
+    Cache cannot serve rows the previous call wrote; also the same batch on a
+    bf16 copy of the pool."""
+    dev = "cuda"
+    c = workloads.config2(device=dev)
+    d = c["decode"]
+    H, Hqk = c["H"], c["Hqk"]
+    B = int(d["last_page_len"].shape[0])
+    o = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
+    idx, ip = d["page_indices"], d["page_indptr"]
+    n_pages = int(c["pool"].shape[0])
+    ends = ip[1:].long()
+    pos = torch.cat([ends - 1, (ends - 2)[ends - 2 >= ip[:-1].long()]])
+    used = torch.unique(idx[pos].long())
+    free_mask = torch.ones(n_pages, dtype=torch.bool, device=dev)
+    free_mask[used] = False
+    free = torch.nonzero(free_mask).flatten()
+    free = free[torch.randperm(free.numel(), generator=torch.Generator().manual_seed(7)).to(dev)]
+    tables = [idx]
+    for r in range(3):
+        lut = torch.arange(n_pages, device=dev)
+        lut[used] = free[r * used.numel():(r + 1) * used.numel()]
+        t = idx.clone()
+        t[pos] = lut[idx[pos].long()].to(idx.dtype)
+        tables.append(t)
+    slot_sets = [gdn.decode_slots(t, ip, d["last_page_len"]) for t in tables]
+    turn = [0]
+
+    def run(pool):
+        r = turn[0] % len(tables)
+        turn[0] += 1
+        gdn.decode_paged(d["q"], d["k"], d["v"], d["g"], d["beta"], pool, tables[r], ip, 1024,
+                         d["last_page_len"], slots=slot_sets[r], out=o)
+    by = decode_bytes(B, H, Hqk)
+    ms, pct = _events_ms(torch, lambda: run(c["pool"]), 40)
+    out = {"workload": "paged decode, 256 sequences (context U[1024,32768], 64 opening a new "
+                       "page), Hqk=16, H=32, page 1024, 8192-page fp32 pool, four page tables "
+                       "with disjoint touched pages in turn",
+           "ms": ms, "ms_p10_p50_p90": pct, "state_GBps": by / (ms / 1e3) / 1e9,
+           "frac_hbm_peak": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": by}
+    pool16 = c["pool"].to(torch.bfloat16)
+    del c["pool"]
+    ms16, _ = _events_ms(torch, lambda: run(pool16), 40)
+    by16 = by - B * H * STATE_BYTES  # state rows at 2 bytes an element
+    out["bf16_pool"] = {"ms": ms16, "state_GBps": by16 / (ms16 / 1e3) / 1e9,
+                        "frac_hbm_peak": by16 / (ms16 / 1e3) / 1e9 / HBM_PEAK_GBPS}
+    del pool16
+    shape = dict(decode=B, Hd=H, Hqkd=Hqk)
+    return out, shape
+
+
+def measure_config3(torch, gdn, workloads):
+    """Long chunked prefill: one sequence, 32 heads, 32768 tokens in 5 calls at
+    7001 / 14500 / 20000 / 27777, checkpoints every 896 tokens into a separate
+    buffer (every other row -1); per call and in total, with the
+    sequence-parallel plan the device picks and as whole sequences."""
+    dev = "cuda"
+    c = workloads.config3(device=dev)
+    H, Hqk = c["H"], c["Hqk"]
+    t_max = max(int(call["q"].shape[0]) for call in c["calls"])
+    # one workspace for the largest call serves every call (sizes only grow)
+    ws = torch.empty(gdn.prefill_workspace_size(t_max, 1, H, Hqk), dtype=torch.uint8, device=dev)
+
+    def one(call, options=None):
+        gdn.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
+                    call["cu_seqlens"], initial_state=c["pool"],
+                    state_indices=call["state_indices"], output_state=c["pool"],
+                    output_state_indices=call["output_state_indices"],
+                    output_final_state=True, state_checkpoints=c["state_checkpoints"],
+                    checkpoint_state_indices=c["checkpoint_state_indices"],
+                    checkpoint_cu_starts=call["checkpoint_cu_starts"],
+                    prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=c["every_n"],
+                    workspace=ws, options=options)
+    calls = c["calls"]
+    per_call = []
+    for call in calls:
+        n = int(call["q"].shape[0])
+        a, e = int(call["start"]), int(call["end"])
+        rows = (1 if a > 0 else 0) + 1 + len([x for x in range(a // 896 + 1, e // 896 + 1)
+                                              if (x - 1) % 2 == 0])
+        by = prefill_bytes(n, H, Hqk, rows)
+        ms, _ = _events_ms(torch, lambda: one(call), 10)
+        per_call.append({"tokens": n, "ms": ms, "prefill_tokens_per_s": n / (ms / 1e3),
+                         "frac_hbm_roofline": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS})
+    T = sum(x["tokens"] for x in per_call)
+    total_by = prefill_bytes(T, H, Hqk, 4 + 5 + 18)
+    ms_total, _ = _events_ms(torch, lambda: [one(call) for call in calls], 5)
+    whole = gdn.Options(prefill_split_chunks=-1)
+    ms_whole, _ = _events_ms(torch, lambda: [one(call, whole) for call in calls], 5)
+    out = {"workload": "one sequence, H=Hqk=32, 32768 tokens in 5 calls (7001/14500/20000/27777), "
+                       "checkpoints every 896 into a separate buffer, every other row -1",
+           "per_call": per_call, "total_ms": ms_total, "prefill_tokens_per_s": T / (ms_total / 1e3),
+           "frac_hbm_roofline": total_by / (ms_total / 1e3) / 1e9 / HBM_PEAK_GBPS,
+           "whole_sequence_total_ms": ms_whole, "speedup_vs_whole": ms_whole / ms_total}
+    del c, ws
+    shape = dict(prefill=[T], H=H, Hqk=Hqk, split_heads=True)
+    return out, shape
 
 
 def hybrid(args, torch, gdn, workloads):
@@ -334,128 +532,34 @@ def hybrid(args, torch, gdn, workloads):
         "slots_ms_per_step": sum(t_sl) / len(t_sl),
         "roofline": roof,
     }
-    if not args.no_side:
-        line["side"] = side_measurements(torch, gdn, workloads, pool, dec0, ps, H, Hqk, t_dc_ms)
-    cpu_inputs = None
-    if not args.no_cpu_baseline:
-        pcpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in pre0.items()}
-        pcpu["H"] = H
-        dcpu = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in dec0.items()}
-        rows = [pcpu["read_rows"][0]] + list(dcpu["read_rows"][:args.cpu_sample_decode])
-        cpu_inputs = (pcpu, dcpu, rows, T, int(c["num_decode"]) + 16)
-    return line, cpu_inputs, pool
+    shapes = {"hybrid": dict(prefill=list(pre0["new"]), H=H, Hqk=Hqk, decode=Bd, Hd=H, Hqkd=Hqk)}
+    return line, shapes
 
 
 def single(args, torch, gdn, workloads):
-    """Prefill-only (config 1), decode-only (config 2) or long chunked prefill (config 3)."""
-    dev = "cuda"
-    E = torch.cuda.Event
-    stream = torch.cuda.current_stream()
-    if args.workload == "prefill":
-        c = workloads.config1(device=dev)
-        p = c["prefill"]
-        H, Hqk = c["H"], c["Hqk"]
-        T = int(p["q"].shape[0])
-        B = int(p["last_page_len"].shape[0])
-        ws = torch.empty(gdn.prefill_workspace_size(T, B, H, Hqk), dtype=torch.uint8, device=dev)
-        o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
-        sl = gdn.prefill_slots(p["cu_seqlens"], p["page_indices"], p["page_indptr"],
-                               p["last_page_len"], 1024)
-
-        def run():
-            gdn.prefill_paged(p["q"], p["k"], p["v"], p["g"], p["beta"], p["cu_seqlens"],
-                              c["pool"], p["page_indices"], p["page_indptr"], 1024,
-                              p["last_page_len"], slots=sl, workspace=ws, out=o)
-        n_io = sum(1 for r in p["read_rows"] if r >= 0) + sum(
-            1 + (a + n) // 1024 - a // 1024 for a, n in zip(p["prefix"], p["new"]))
-        work_bytes = prefill_bytes(T, H, Hqk, n_io)
-        desc = "paged prefill B=8, H=Hqk=16, page 1024, shared prefixes"
-        unit_val = lambda ms: T / (ms / 1e3)  # noqa: E731
-        unit = "prefill tokens/s"
-    elif args.workload == "decode":
-        c = workloads.config2(device=dev)
-        d = c["decode"]
-        H, Hqk = c["H"], c["Hqk"]
-        B = int(d["last_page_len"].shape[0])
-        o = torch.empty(B, H, D, dtype=torch.bfloat16, device=dev)
-        # Four page-table variants whose touched pages (the last two of every
-        # sequence) are disjoint, used in turn, so that the 256 MB Infinity
-        # Cache cannot serve rows the previous call just wrote.
-        idx, ip = d["page_indices"], d["page_indptr"]
-        n_pages = int(c["pool"].shape[0])
-        ends = ip[1:].long()
-        pos = torch.cat([ends - 1, (ends - 2)[ends - 2 >= ip[:-1].long()]])
-        used = torch.unique(idx[pos].long())
-        free_mask = torch.ones(n_pages, dtype=torch.bool, device=dev)
-        free_mask[used] = False
-        free = torch.nonzero(free_mask).flatten()
-        free = free[torch.randperm(free.numel(), generator=torch.Generator().manual_seed(7)).to(dev)]
-        tables = [idx]
-        for r in range(3):
-            lut = torch.arange(n_pages, device=dev)
-            lut[used] = free[r * used.numel():(r + 1) * used.numel()]
-            t = idx.clone()
-            t[pos] = lut[idx[pos].long()].to(idx.dtype)
-            tables.append(t)
-        slot_sets = [gdn.decode_slots(t, ip, d["last_page_len"]) for t in tables]
-        turn = [0]
-
-        def run():
-            r = turn[0] % len(tables)
-            turn[0] += 1
-            gdn.decode_paged(d["q"], d["k"], d["v"], d["g"], d["beta"], c["pool"],
-                             tables[r], ip, 1024, d["last_page_len"], slots=slot_sets[r], out=o)
-        work_bytes = decode_bytes(B, H, Hqk)
-        desc = ("paged decode B=256, Hqk=16, H=32, page 1024, 25% new-page tokens, four page "
-                "tables with disjoint touched pages in turn")
-        unit_val = lambda ms: work_bytes / (ms / 1e3) / 1e9  # noqa: E731
-        unit = "decode state GB/s"
-    else:
-        c = workloads.config3(device=dev)
-        H, Hqk = c["H"], c["Hqk"]
-        T = 32768
-        calls = c["calls"]
-        ws = torch.empty(gdn.prefill_workspace_size(8192, 1, H, Hqk), dtype=torch.uint8,
-                         device=dev)
-
-        def run():
-            for call in calls:
-                gdn.prefill(call["q"], call["k"], call["v"], call["g"], call["beta"],
-                            call["cu_seqlens"], initial_state=c["pool"],
-                            state_indices=call["state_indices"], output_state=c["pool"],
-                            output_state_indices=call["output_state_indices"],
-                            output_final_state=True, state_checkpoints=c["state_checkpoints"],
-                            checkpoint_state_indices=c["checkpoint_state_indices"],
-                            checkpoint_cu_starts=call["checkpoint_cu_starts"],
-                            prefix_lens=call["prefix_lens"], checkpoint_every_n_tokens=896,
-                            workspace=ws)
-        work_bytes = prefill_bytes(T, H, Hqk, 5 + 4 + 18)
-        desc = "long chunked prefill B=1, H=32, 32768 tokens in 5 calls, checkpoints every 896"
-        unit_val = lambda ms: T / (ms / 1e3)  # noqa: E731
-        unit = "prefill tokens/s"
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(args.steps)]
+    """One of the other workloads alone: paged prefill (config 1), paged
+    decode (config 2) or the long chunked prefill (config 3)."""
+    fn = {"prefill": measure_config1, "decode": measure_config2, "long": measure_config3}
     t0 = time.perf_counter()
-    for a, b in evs:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
+    res, _ = fn[args.workload](torch, gdn, workloads)
     wall = time.perf_counter() - t0
-    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    ach = work_bytes / (ms / 1e3) / 1e9
+    if args.workload == "prefill":
+        r = res["slots_passed"]
+        val, unit, ms, frac = r["prefill_tokens_per_s"], "prefill tokens/s", r["ms"], r["frac_hbm_roofline"]
+    elif args.workload == "decode":
+        val, unit, ms, frac = res["state_GBps"], "decode state GB/s", res["ms"], res["frac_hbm_peak"]
+    else:
+        val, unit, ms, frac = res["prefill_tokens_per_s"], "prefill tokens/s", res["total_ms"], res["frac_hbm_roofline"]
     line = {
-        "metric": METRIC, "value": unit_val(ms), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1000 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16/fp32",
-        "data": "synthetic", "config": {"workload": desc},
-        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBPS, "traffic": None,
-                     "per_launch_bytes": work_bytes, "avg_launch_ms": ms},
+        "metric": METRIC, "value": val, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16/fp32", "data": "synthetic",
+        "config": {"workload": res["workload"]},
+        "roofline": {"bound": "hbm", "achieved": frac * HBM_PEAK_GBPS, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": frac, "traffic": None, "avg_launch_ms": ms},
+        "detail": res, "wall_s": wall,
     }
-    return line, None, None
+    return line
 
 
 def main():
@@ -487,18 +591,22 @@ def main():
         torch.cuda.synchronize()
         copy_gbps = 2 * n * reps / (a.elapsed_time(b) / 1e3) / 1e9
         del src, dst
-    if args.workload == "hybrid":
-        line, cpu_inputs, pool = hybrid(args, torch, gdn, workloads)
-    else:
-        line, cpu_inputs, pool = single(args, torch, gdn, workloads)
-    if cpu_inputs is not None:
-        pcpu, dcpu, rows, T, ndec = cpu_inputs
-        import numpy as np  # noqa: F401
-        # The pool rows the sample reads, copied before any timing mutated them?  The
-        # timed steps rewrote them; the oracle's speed does not depend on their values.
-        pool_rows = {int(r): pool[int(r)].cpu().numpy() for r in rows if int(r) >= 0}
-        line["cpu_baseline"] = cpu_baseline(pcpu, dcpu, pool_rows, args.cpu_sample_tokens,
-                                            args.cpu_sample_decode, args.layers, T, ndec)
+    if args.workload != "hybrid":
+        print(json.dumps(single(args, torch, gdn, workloads)), flush=True)
+        return
+    line, shapes = hybrid(args, torch, gdn, workloads)
+    torch.cuda.empty_cache()
+    if not args.no_side:
+        # the other workloads, each alone after the step (their inputs made
+        # and freed in turn)
+        side = {}
+        for name, fn in (("config1_prefill", measure_config1), ("config2_decode", measure_config2),
+                         ("config3_long_prefill", measure_config3)):
+            side[name], shapes[name] = fn(torch, gdn, workloads)
+            torch.cuda.empty_cache()
+        line["side"] = side
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(shapes, args.layers)
     if copy_gbps is not None:
         line["copy_GBps"] = copy_gbps
     print(json.dumps(line), flush=True)
