@@ -31,9 +31,12 @@
 //   straight out of MFMA accumulators (computed as P^T blocks), K^T fragments
 //   come from K fragments times a 0/1 selection operand, and eight waves each
 //   advance 16 rows of the state, whose fp32 transpose lives in MFMA
-//   accumulators (the layout the next chunk's B operand needs).  fp32
-//   operands are split into bf16 hi + lo (3 passes when both sides are fp32,
-//   2 when one side is exact bf16), which keeps ~2^-17 relative accuracy.
+//   accumulators (the layout the next chunk's B operand needs).  The
+//   products that feed the state keep ~2^-17 relative accuracy by splitting
+//   fp32 operands into bf16 hi + lo (3 passes when both sides are fp32, 2
+//   when one side is exact bf16): E = T R and the state update.  Y = K S^T
+//   and the output-only products (Z = S Q^T, P E) take S and E rounded to
+//   bf16 in one pass.
 //   The next chunk's tiles load straight from global memory into
 //   double-buffered LDS while the current one computes.
 #include "gdn_internal.h"
@@ -43,6 +46,8 @@ namespace gdn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// chunk decay exp(G_last) above which Y = K S^T takes a second (lo) pass
+constexpr float kYLoGamma = 0x1p-10f;
 constexpr int kTileWords = 4 * 4 * kFragElems;  // 64 x 128 bf16, fragment order
 constexpr int kKtWordsL = 8 * 2 * kFragElems;   // K^T fragments
 constexpr int kMatFrag = 8 * kFragElems;        // one 64x64 operand (8 fragments)
@@ -745,16 +750,40 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     // flight (a chain of dependent MFMAs issues at about a third of the
     // rate), and each step's operand fragments are read while the previous
     // step multiplies.
+    // S as bf16 operands: Shi (rounded) for Y = K S^T and Z = S Q^T, plus
+    // Slo = S - Shi for a second Y pass in chunks with weak decay.  Y enters
+    // the state through R = V - gamma Y and E = T R, whose rows reach the
+    // chunk's end state scaled by exp(G_last - G_t): every row's Y error
+    // arrives there scaled by gamma_last = exp(G_last), the chunk's whole
+    // decay.  Below 2^-10 the single pass's 2^-9 error is out of sight
+    // (measured against the fp64 oracle: hybrid-step states 4.5e-6 either
+    // way); above it -- weak or no decay, short tail chunks -- the second
+    // pass keeps states near 1e-5 (one pass: 6.9e-5 with decay / 10, over
+    // 1e-3 with none).  A single-pass E or state update would cost 0.7e-3 ..
+    // 2.4e-3 at any decay, so those always take hi/lo passes.
+    const bool y_lo = __builtin_amdgcn_readfirstlane(
+        __builtin_bit_cast(int, sc[2][kChunk - 1]) > __builtin_bit_cast(int, kYLoGamma));
     bf16x8 Shi[4], Slo[4];
+    if (y_lo) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float v[8];
+      for (int ks = 0; ks < 4; ++ks) {
+        float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = accS[2 * ks + (j >> 2)][j & 3];
-      split8(v, Shi[ks], Slo[ks]);
+        for (int j = 0; j < 8; ++j) v[j] = accS[2 * ks + (j >> 2)][j & 3];
+        split8(v, Shi[ks], Slo[ks]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = accS[2 * ks + (j >> 2)][j & 3];
+        Shi[ks] = round8(v);
+        Slo[ks] = Shi[ks];  // unused
+      }
     }
 
-    // Y = K S^T (hi and lo passes)
+    // Y = K S^T (the lo pass only where the decay is weak)
     f32x4 y[4];
     bf16x8 vf[4];
     {
@@ -775,8 +804,10 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
         sched_fence();
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Shi[ks], y[mt]);
+        if (y_lo) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Slo[ks], y[mt]);
+          for (int mt = 0; mt < 4; ++mt) y[mt] = mfma16x16x32(kf[ks & 1][mt], Slo[ks], y[mt]);
+        }
         sched_fence();
       }
     }
