@@ -100,6 +100,15 @@ typedef struct {
   int32_t decode_waves;
   int32_t decode_stream_per_cu;
   int32_t decode_stream_grid;
+  /* Debug validation (NULL = off, the default: nothing extra runs).  A
+   * device int32: gdn_prefill_paged and gdn_decode_paged first run
+   * gdn_check_paged into it (against a pool of check_num_pages rows), and
+   * every later kernel of the call returns without reading or writing
+   * anything when the word holds an error bit other than
+   * GDN_CHECK_NOT_CHECKED; the caller reads the word when it likes (the
+   * call itself never synchronizes). */
+  int32_t* check_error_word;
+  int32_t check_num_pages;
 } gdn_options_t;
 
 /* Head geometry shared by every call, and the call's launch choices. */
@@ -218,6 +227,38 @@ int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, cons
                       const int32_t* page_indptr, const int32_t* last_page_len,
                       int32_t page_size, const gdn_prefill_slots_t* slots, void* o,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_check_paged -- debug validation of a paged batch, on the device in one
+ * launch and without a host synchronization: writes to *error_word a mask of
+ * the GDN_CHECK_* bits below (0 = nothing found).  The page says page tables
+ * hold real page ids and slots are not validated against them, and that a
+ * row one sequence writes must not be touched by another sequence of the
+ * call (flashinfer.gdn_paged, "Page table", "Slot arguments"); this call
+ * checks what the paged calls take on trust.
+ *   cu_seqlens [num_seqs+1] for a prefill batch, NULL for a decode batch.
+ *   page_indptr [num_seqs+1] and last_page_len [num_seqs] are read whole,
+ *   page_indices for its page_indptr[num_seqs] entries (once page_indptr is
+ *   found well formed); num_pages = rows of the pool.
+ * The row check covers batches of up to 2048 sequences touching up to 4096
+ * pages in all; beyond that it is skipped and GDN_CHECK_NOT_CHECKED is set.
+ * Errors: GDN_EINVAL for null pointers, num_seqs < 1, page_size not a
+ * positive multiple of 64, num_pages < 1.
+ */
+enum {
+  GDN_CHECK_INDPTR = 1,         /* page_indptr[0] != 0, decreasing, or a sequence with no page */
+  GDN_CHECK_LAST_PAGE_LEN = 2,  /* last_page_len outside 1 .. page_size */
+  GDN_CHECK_TOKENS = 4,         /* prefill: cu_seqlens[0] != 0, or a sequence with a negative
+                                   count or more new tokens than it holds; decode: a sequence
+                                   holding no token before the decoded one */
+  GDN_CHECK_PAGE_ID = 8,        /* a page id outside 0 .. num_pages - 1 */
+  GDN_CHECK_SHARED_ROW = 16,    /* a row one sequence writes is read or written by another */
+  GDN_CHECK_NOT_CHECKED = 32    /* batch beyond the row check's size: that check skipped */
+};
+int gdn_check_paged(const int32_t* cu_seqlens, const int32_t* page_indices,
+                    const int32_t* page_indptr, const int32_t* last_page_len, int32_t num_seqs,
+                    int32_t page_size, int32_t num_pages, int32_t* error_word,
+                    hipStream_t stream);
 
 /*
  * gdn_prefill_paged_noalloc -- gdn_prefill_paged for callers that cannot

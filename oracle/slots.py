@@ -96,3 +96,75 @@ def checkpoint_count(prefix: int, new_len: int, every_n: int) -> int:
     """Checkpoints a call takes: positions ``prefix + n`` (n = 1..new_len)
     that are multiples of ``every_n``, counted one by one."""
     return sum(1 for n in range(1, new_len + 1) if (prefix + n) % every_n == 0)
+
+
+# Validity of a paged batch: what the paged calls take on trust (the page
+# table holds real page ids, never -1 padding; a row one sequence writes is
+# touched by no other sequence of the call), as bits of a mask.  The bit
+# values are this library's convention.
+CHECK_INDPTR = 1         # indptr[0] != 0, decreasing, or a sequence with no page
+CHECK_LAST_PAGE_LEN = 2  # last_page_len outside 1 .. page_size
+CHECK_TOKENS = 4         # prefill: cu[0] != 0, negative or too many new tokens;
+                         # decode: no token before the decoded one
+CHECK_PAGE_ID = 8        # a page id outside 0 .. num_pages - 1
+CHECK_SHARED_ROW = 16    # a row one sequence writes is read or written by another
+
+
+def touched_rows(pages: Sequence[int], last_page_len: int, page_size: int, new_len=None):
+    """(rows read, rows written) by one sequence of a paged call: a prefill
+    (``new_len`` given) reads the page holding its last prefix token and writes
+    every page ending after its prefix; a decode reads the previous page when
+    the token opens a new one, else the last page, and writes the last page."""
+    n = len(pages)
+    total = (n - 1) * page_size + last_page_len
+    if new_len is None:
+        return ({pages[-2] if last_page_len == 1 else pages[-1]}, {pages[-1]})
+    p = total - new_len
+    reads = {pages[(p - 1) // page_size]} if p > 0 else set()
+    writes = {pages[j] for j in range(p // page_size, n)} if new_len > 0 else set()
+    return reads, writes
+
+
+def check_paged(page_indices, page_indptr, last_page_len, page_size: int, num_pages: int,
+                cu_seqlens=None) -> int:
+    """Mask of the validity rules a paged batch breaks (0: none).  Structure
+    first; page ids and shared rows only once the structure holds, as the
+    ranges are unknown otherwise."""
+    ptr = [int(x) for x in page_indptr]
+    lpl = [int(x) for x in last_page_len]
+    B = len(lpl)
+    cu = None if cu_seqlens is None else [int(x) for x in cu_seqlens]
+    bits = 0
+    if ptr[0] != 0:
+        bits |= CHECK_INDPTR
+    for b in range(B):
+        n = ptr[b + 1] - ptr[b]
+        if n <= 0:
+            bits |= CHECK_INDPTR
+            continue
+        if not 1 <= lpl[b] <= page_size:
+            bits |= CHECK_LAST_PAGE_LEN
+        total = (n - 1) * page_size + lpl[b]
+        if cu is not None:
+            L = cu[b + 1] - cu[b]
+            if L < 0 or L > total:
+                bits |= CHECK_TOKENS
+        elif total < 2:
+            bits |= CHECK_TOKENS
+    if cu is not None and cu[0] != 0:
+        bits |= CHECK_TOKENS
+    if bits:
+        return bits
+    idx = [int(x) for x in page_indices[:ptr[B]]]
+    if any(not 0 <= x < num_pages for x in idx):
+        return CHECK_PAGE_ID
+    touched = []
+    for b in range(B):
+        pages = idx[ptr[b]:ptr[b + 1]]
+        L = None if cu is None else cu[b + 1] - cu[b]
+        touched.append(touched_rows(pages, lpl[b], page_size, L))
+    for b, (_, wb) in enumerate(touched):
+        for c, (rc, wc) in enumerate(touched):
+            if c != b and wb & (rc | wc):
+                return CHECK_SHARED_ROW
+    return 0

@@ -10,7 +10,10 @@ from ._lib import (  # noqa: F401
     GDNError,
     Options,
     PrefillSlots,
+    CHECK_BITS,
     block_table_to_csr,
+    check_paged,
+    checked,
     csr_to_block_table,
     decode,
     decode_paged,

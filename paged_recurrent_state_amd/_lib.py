@@ -35,10 +35,14 @@ class Options(C.Structure):
     split, m > 0 segments of m chunks.  prefill_tile_waves: 0/8 whole heads,
     4/2/1 V-tiles.  decode_waves: 2/4/8/16 one-pair decode width.
     decode_stream_per_cu: streaming decode workgroups per CU (-1 off).
-    decode_stream_grid: streaming decode grid."""
+    decode_stream_grid: streaming decode grid.
+    check_error_word / check_num_pages: device address of an int32 and the
+    pool's row count; the paged calls then validate their batch first and do
+    nothing else when it fails (see ``checked``)."""
     _fields_ = [("prefill_split_chunks", C.c_int32), ("prefill_tile_waves", C.c_int32),
                 ("decode_waves", C.c_int32), ("decode_stream_per_cu", C.c_int32),
-                ("decode_stream_grid", C.c_int32)]
+                ("decode_stream_grid", C.c_int32), ("check_error_word", C.c_void_p),
+                ("check_num_pages", C.c_int32)]
 
 
 class Dims(C.Structure):
@@ -76,7 +80,20 @@ class DecodeSlots(NamedTuple):
     output_state_indices: torch.Tensor
 
 
-EXPORTS = ["gdn_prefill_slots", "gdn_decode_slots", "gdn_prefill_workspace_size",
+CHECK_BITS = {1: "GDN_CHECK_INDPTR", 2: "GDN_CHECK_LAST_PAGE_LEN", 4: "GDN_CHECK_TOKENS",
+              8: "GDN_CHECK_PAGE_ID", 16: "GDN_CHECK_SHARED_ROW", 32: "GDN_CHECK_NOT_CHECKED"}
+
+
+def checked(word: torch.Tensor, num_pages: int, **fields) -> Options:
+    """Options that make the paged calls validate their batch into ``word`` (a [1]
+    int32 device tensor, kept alive by the caller) against a pool of ``num_pages``
+    rows; other fields as in ``Options``."""
+    if word.dtype != torch.int32 or word.numel() < 1 or not word.is_cuda:
+        raise ValueError("word must be an int32 device tensor")
+    return Options(check_error_word=word.data_ptr(), check_num_pages=int(num_pages), **fields)
+
+
+EXPORTS = ["gdn_check_paged", "gdn_prefill_slots", "gdn_decode_slots", "gdn_prefill_workspace_size",
            "gdn_prefill_paged", "gdn_prefill_paged_noalloc", "gdn_decode_paged", "gdn_prefill", "gdn_decode",
            "gdn_block_table_to_csr", "gdn_csr_to_block_table", "gdn_last_error", "gdn_version"]
 
@@ -95,6 +112,7 @@ def load():
     lib = C.CDLL(_LIB_PATH)
     P, I32, I64, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     sig = {
+        "gdn_check_paged": (C.c_int, [P, P, P, P, I32, I32, I32, P, P]),
         "gdn_prefill_slots": (C.c_int, [P, P, P, P, I32, I32, C.POINTER(_PrefillSlotsC), P]),
         "gdn_decode_slots": (C.c_int, [P, P, P, I32, C.POINTER(_DecodeSlotsC), P]),
         "gdn_prefill_workspace_size": (SZ, [I64, I32, C.POINTER(Dims)]),
@@ -247,6 +265,27 @@ def prefill_slots(cu_seqlens, page_indices, page_indptr, last_page_len, page_siz
                                  _ptr(last_page_len), B, int(page_size), C.byref(sc),
                                  _stream(dev)))
     return out
+
+
+def check_paged(page_indices, page_indptr, last_page_len, page_size: int, num_pages: int,
+                cu_seqlens=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Validate a paged batch on the device (prefill when ``cu_seqlens`` is given,
+    else decode); returns a [1] int32 device tensor with the GDN_CHECK_* bits
+    found (0: none).  No host synchronization."""
+    lib = load()
+    dev = page_indptr.device
+    for t, nm in ((page_indices, "page_indices"), (page_indptr, "page_indptr"),
+                  (last_page_len, "last_page_len")):
+        _need(t, nm, torch.int32, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    word = out if out is not None else torch.empty(1, dtype=torch.int32, device=dev)
+    B = last_page_len.shape[0]
+    idx = page_indices if page_indices.numel() else page_indptr
+    _check(lib.gdn_check_paged(_ptr(cu_seqlens), _ptr(idx), _ptr(page_indptr),
+                               _ptr(last_page_len), B, int(page_size), int(num_pages), _ptr(word),
+                               _stream(dev)))
+    return word
 
 
 def decode_slots(page_indices, page_indptr, last_page_len,

@@ -63,15 +63,19 @@ struct Opts {
   int split;   // gdn_options_t.prefill_split_chunks
   int waves;   // recurrence workgroup width
   DecodeShape dec;
+  int32_t* check;  // debug check word (null: no check)
+  int check_pages;
 };
 
 Opts get_opts(const gdn_dims_t* d) {
-  Opts o{0, 8, DecodeShape{0, 0, 0}};
+  Opts o{0, 8, DecodeShape{0, 0, 0}, nullptr, 0};
   if (d && d->options) {
     const gdn_options_t* x = d->options;
     o.split = x->prefill_split_chunks;
     o.waves = x->prefill_tile_waves ? x->prefill_tile_waves : 8;
     o.dec = DecodeShape{x->decode_waves, x->decode_stream_per_cu, x->decode_stream_grid};
+    o.check = x->check_error_word;
+    o.check_pages = x->check_num_pages;
   }
   return o;
 }
@@ -163,6 +167,8 @@ int check_opts(const gdn_dims_t* d) {
     return fail(GDN_EINVAL, "options.decode_waves must be 0, 2, 4, 8 or 16 (got %d)", dw);
   if (x->decode_stream_per_cu < -1 || x->decode_stream_grid < 0)
     return fail(GDN_EINVAL, "options.decode_stream_per_cu must be >= -1 and decode_stream_grid >= 0");
+  if (x->check_error_word && x->check_num_pages < 1)
+    return fail(GDN_EINVAL, "options.check_error_word needs check_num_pages >= 1");
   return GDN_OK;
 }
 
@@ -213,7 +219,7 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
                 const SlotsDev& sd, const WsLayout& L, void* ws, const void* init,
                 int64_t init_stride, void* out, int64_t out_stride, void* ckpt,
                 int64_t ckpt_stride, const void* ckpt_idx, int ckpt_idx64, int ckpt_every,
-                void* o, hipStream_t stream) {
+                void* o, hipStream_t stream, const int32_t* guard = nullptr) {
   PrefillParams pp;
   pp.q = (const u16*)q;
   pp.k = (const u16*)k;
@@ -258,6 +264,7 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.ws_state_stride = (int64_t)d->num_v_heads * kDim * kDim;
   pp.vseq = nullptr;
   pp.vcount = nullptr;
+  pp.guard = guard;
   if (int rc = launched(launch_prefill(pp, L.nc, stream), "prefill kernels")) return rc;
   return ok();
 }
@@ -325,6 +332,12 @@ int prefill_paged_impl(const gdn_dims_t* dims, const void* q, const void* k, con
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255))
     return fail(GDN_EWORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", L.total,
                 workspace_bytes);
+  const Opts opt = get_opts(dims);
+  if (opt.check &&
+      launched(launch_check_paged(cu_seqlens, page_indices, page_indptr, last_page_len, num_seqs,
+                                  page_size, opt.check_pages, opt.check, stream),
+               "check kernel"))
+    return GDN_ELAUNCH;
   SlotsDev sd;
   if (slots) {
     sd = SlotsDev{slots->state_indices, slots->output_state_indices, slots->checkpoint_cu_starts,
@@ -335,7 +348,7 @@ int prefill_paged_impl(const gdn_dims_t* dims, const void* q, const void* k, con
                                                last_page_len, num_seqs, page_size,
                                                (int32_t*)sd.read, (int32_t*)sd.write,
                                                (int32_t*)sd.ckpt_start, (int32_t*)sd.prefix,
-                                               (int32_t*)sd.chunk_start, stream),
+                                               (int32_t*)sd.chunk_start, opt.check, stream),
                           "prefill slot kernel"))
       return rc;
   }
@@ -344,7 +357,7 @@ int prefill_paged_impl(const gdn_dims_t* dims, const void* q, const void* k, con
   // buffers and a checkpoint every page_size tokens into page_indices.
   return run_prefill(dims, q, k, v, g, beta, cu_seqlens, num_seqs, sd, L, workspace, state_pool,
                      pool_row_stride, state_pool, pool_row_stride, state_pool, pool_row_stride,
-                     page_indices, 0, page_size, o, stream);
+                     page_indices, 0, page_size, o, stream, opt.check);
 }
 
 }  // namespace
@@ -396,7 +409,7 @@ int gdn_prefill_slots(const int32_t* cu_seqlens, const int32_t* page_indices,
                                              num_seqs, page_size, out->state_indices,
                                              out->output_state_indices,
                                              out->checkpoint_cu_starts, out->prefix_lens,
-                                             out->chunk_starts, stream),
+                                             out->chunk_starts, nullptr, stream),
                         "prefill slot kernel"))
     return rc;
   return ok();
@@ -452,6 +465,22 @@ int gdn_csr_to_block_table(const int32_t* page_indptr, const int32_t* page_indic
                                                   num_seqs, page_size, max_blocks, block_tables,
                                                   row_stride, ctx_lens, bad_rows, stream),
                         "CSR to block table"))
+    return rc;
+  return ok();
+}
+
+int gdn_check_paged(const int32_t* cu_seqlens, const int32_t* page_indices,
+                    const int32_t* page_indptr, const int32_t* last_page_len, int32_t num_seqs,
+                    int32_t page_size, int32_t num_pages, int32_t* error_word,
+                    hipStream_t stream) {
+  if (num_seqs < 1) return fail(GDN_EINVAL, "num_seqs must be >= 1 (got %d)", num_seqs);
+  if (int rc = check_page_size(page_size)) return rc;
+  if (num_pages < 1) return fail(GDN_EINVAL, "num_pages must be >= 1 (got %d)", num_pages);
+  if (!page_indices || !page_indptr || !last_page_len || !error_word)
+    return fail(GDN_EINVAL, "page table and error_word must not be NULL");
+  if (int rc = launched(launch_check_paged(cu_seqlens, page_indices, page_indptr, last_page_len,
+                                           num_seqs, page_size, num_pages, error_word, stream),
+                        "check kernel"))
     return rc;
   return ok();
 }
@@ -512,6 +541,16 @@ int gdn_decode_paged(const gdn_dims_t* dims, const void* q, const void* k, const
   dp.init_stride = pool_row_stride;
   dp.out = state_pool;
   dp.out_stride = pool_row_stride;
+  const Opts opt = get_opts(dims);
+  if (opt.check) {
+    if (!page_indices || !page_indptr || !last_page_len)
+      return fail(GDN_EINVAL, "the check needs the page table");
+    if (launched(launch_check_paged(nullptr, page_indices, page_indptr, last_page_len, num_seqs,
+                                    page_size, opt.check_pages, opt.check, stream),
+                 "check kernel"))
+      return GDN_ELAUNCH;
+    dp.guard = opt.check;
+  }
   if (slots) {
     if (!slots->initial_state_indices || !slots->output_state_indices)
       return fail(GDN_EINVAL, "both slot arrays must be given");

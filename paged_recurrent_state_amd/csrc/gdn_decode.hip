@@ -201,6 +201,7 @@ __device__ __forceinline__ void decode_update(const DecodeParams& p, int b, int 
 // One (sequence, v-head) per workgroup.
 template <bool BF16, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams p) {
+  if (guarded(p.guard)) return;
   const int b = blockIdx.x / p.H, h = blockIdx.x - b * p.H;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4;  // row within the wave's 4 rows of a step
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(const DecodePara
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   int it = blockIdx.x;
-  if (it >= items) return;
+  if (it >= items || guarded(p.guard)) return;
   DecRows r0 = decode_rows(p, it / p.H);
   DecItem<BF16, NW> cur;
   decode_load(p, it / p.H, it % p.H, r0.rd, wid, g, c, cur);

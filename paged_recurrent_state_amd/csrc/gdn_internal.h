@@ -98,6 +98,7 @@ struct PrefillParams {
   int64_t ws_state_stride;
   const int32_t* vseq;     // the records this launch walks (null: whole sequences)
   const int32_t* vcount;   // how many of them are real
+  const int32_t* guard;    // debug check word (null: none); nonzero error bits: return at once
 };
 
 struct DecodeParams {
@@ -127,15 +128,19 @@ struct DecodeParams {
   int64_t init_stride;
   void* out;
   int64_t out_stride;
+  const int32_t* guard;  // debug check word (null: none); nonzero error bits: return at once
 };
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_prefill_slots(const int32_t* cu, const int32_t* idx, const int32_t* ptr,
                                 const int32_t* lpl, int B, int page_size, int32_t* read,
                                 int32_t* write, int32_t* ckpt, int32_t* prefix,
-                                int32_t* chunk_start, hipStream_t s);
+                                int32_t* chunk_start, const int32_t* guard, hipStream_t s);
 hipError_t launch_decode_slots(const int32_t* idx, const int32_t* ptr, const int32_t* lpl,
                                int B, int32_t* read, int32_t* write, hipStream_t s);
+hipError_t launch_check_paged(const int32_t* cu, const int32_t* idx, const int32_t* ptr,
+                              const int32_t* lpl, int B, int page_size, int num_pages,
+                              int32_t* word, hipStream_t s);
 hipError_t launch_general_slots(const int32_t* cu, int B, const void* sidx, const void* oidx,
                                 const void* cstart, const void* plen, int idx64, int has_init,
                                 int write_final, int32_t* read, int32_t* write, int32_t* ckpt,
@@ -167,6 +172,10 @@ int current_device();
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// A debug check word holding an error (any bit but "not checked", 32): the
+// kernels of a checked call then return before touching memory.
+__device__ __forceinline__ bool guarded(const int32_t* g) { return g && (*g & ~32) != 0; }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -276,6 +276,7 @@ struct WySmem {
 
 __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   __shared__ __align__(16) WySmem sm;
+  if (guarded(p.guard)) return;
   const int c = blockIdx.x / p.H;
   const int h = head_of(blockIdx.x - c * p.H, p.H, p.group);
   const int tid = threadIdx.x;
@@ -595,6 +596,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   constexpr int kTiles = 8 / NW;  // V-tiles per head
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RecSmem& sm = *reinterpret_cast<RecSmem*>(smem_raw);
+  if (guarded(p.guard)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
@@ -1378,6 +1380,7 @@ __device__ void split_plan(const PrefillParams& p) {
 // plan too (the two read the slot rows only, not each other's output): one
 // workgroup of kPlanTile threads, one launch.
 __global__ __launch_bounds__(kPlanTile) void plan_kernel(const PrefillParams p) {
+  if (guarded(p.guard)) return;
   plan_body(p.cu_seqlens, p.slots.prefix, p.slots.chunk_start, p.num_seqs, p.num_chunk_slots,
             p.order, p.chunk_tab, (uint32_t*)p.zero_row);
   if (p.split_mode != kSplitOff) split_plan(p);
@@ -1407,6 +1410,7 @@ struct ScanSmem {
 __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
+  if (guarded(p.guard)) return;
   const int j = blockIdx.x;
   const int rb = (j >> 3) & 7, bh = 8 * (j >> 6) + (j & 7);
   if (bh >= p.num_seqs * p.H) return;  // the last group of 8 heads may be partial

@@ -29,7 +29,8 @@ __global__ __launch_bounds__(kScanThreads) void prefill_slots_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ ptr, const int32_t* __restrict__ lpl, int B, int ps,
     int32_t* __restrict__ read, int32_t* __restrict__ write, int32_t* __restrict__ ckpt,
-    int32_t* __restrict__ prefix, int32_t* __restrict__ chunk_start) {
+    int32_t* __restrict__ prefix, int32_t* __restrict__ chunk_start, const int32_t* guard) {
+  if (guarded(guard)) return;
   int carry = 0;
   for (int base = 0; base < B; base += kScanThreads) {
     const int b = base + (int)threadIdx.x;
@@ -103,10 +104,10 @@ __global__ __launch_bounds__(kScanThreads) void general_slots_kernel(
 hipError_t launch_prefill_slots(const int32_t* cu, const int32_t* idx, const int32_t* ptr,
                                 const int32_t* lpl, int B, int page_size, int32_t* read,
                                 int32_t* write, int32_t* ckpt, int32_t* prefix,
-                                int32_t* chunk_start, hipStream_t s) {
+                                int32_t* chunk_start, const int32_t* guard, hipStream_t s) {
   if (B == 0) return hipSuccess;
   prefill_slots_kernel<<<1, kScanThreads, 0, s>>>(cu, idx, ptr, lpl, B, page_size, read, write,
-                                                  ckpt, prefix, chunk_start);
+                                                  ckpt, prefix, chunk_start, guard);
   return hipGetLastError();
 }
 

@@ -227,3 +227,18 @@ def test_bad_state_dtype(lib):
     d.state_dtype = 2
     assert _prefill_paged(lib, d) == -1
     assert b"state_dtype" in lib.gdn_last_error()
+
+
+def test_check_rejects_bad_args(lib):
+    fake = C.c_void_p(0x1000)  # never dereferenced: the call fails before launching
+    chk = lambda B=1, ps=64, n=8, word=fake, idx=fake: lib.gdn_check_paged(  # noqa: E731
+        None, idx, fake, fake, B, ps, n, word, None)
+    assert chk(B=0) == -1
+    assert chk(ps=100) == -1
+    assert chk(n=0) == -1
+    assert chk(word=None) == -1
+    assert chk(idx=None) == -1
+    # the paged calls' check option needs the pool's row count
+    o = _lib.Options(check_error_word=0x1000, check_num_pages=0)
+    assert _prefill_paged(lib, dims(options=o)) == -1
+    assert b"check_num_pages" in lib.gdn_last_error()
