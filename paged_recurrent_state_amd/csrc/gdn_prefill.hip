@@ -277,8 +277,15 @@ struct WySmem {
 __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   __shared__ __align__(16) WySmem sm;
   if (guarded(p.guard)) return;
-  const int c = blockIdx.x / p.H;
-  const int h = head_of(blockIdx.x - c * p.H, p.H, p.group);
+  // Workgroups go to the 8 XCDs round-robin by block index: block b runs on
+  // XCD b % 8, and every v-head of chunk slot c runs on XCD c % 8, so the
+  // cache lines of g and beta (all heads of a token side by side) and of K
+  // (heads of a q/k group) are fetched into one L2 per chunk, not eight.
+  const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
+  const int cg = r / p.H;
+  const int c = 8 * cg + xcd;
+  if (c >= p.num_chunk_slots) return;  // the grid is rounded up to 8 chunk slots
+  const int h = r - cg * p.H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
@@ -781,7 +788,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = accS[2 * ks + (j >> 2)][j & 3];
         Shi[ks] = round8(v);
-        Slo[ks] = Shi[ks];  // unused
+        Slo[ks] = Shi[ks];  // not read on this path (keeps it initialised)
       }
     }
 
@@ -1549,7 +1556,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   plan_kernel<<<1, kPlanTile, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  wy_kernel<<<(unsigned)(num_chunk_slots * p.H), kWyThreads, 0, s>>>(p);
+  wy_kernel<<<(unsigned)((num_chunk_slots + 7) / 8 * 8 * p.H), kWyThreads, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Whole heads per workgroup (8 waves) by default.  Narrower V-tiles (4, 2
