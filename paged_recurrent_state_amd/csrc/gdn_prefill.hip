@@ -162,19 +162,35 @@ struct Seq {
 // counter only, and hidden from the compiler they do not make it drain
 // every outstanding LDS read at each later wait.  Their completion is
 // awaited explicitly (wait_loads, then a barrier) before the data is read.
+// NT: the non-temporal policy, for the last read of a tile or record (the
+// stores of o, records and states carry it too); the streams then leave the
+// caches to what is read again: the g and beta lines, the chunk table, the K
+// tiles the intra-chunk step reads before the recurrence does, and the tiles
+// a sequence-parallel first pass reads again in its second pass.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
 __device__ __forceinline__ void lds_load16(u16* dst_block, const void* src) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst_block);
   // (one wait state between the M0 write and the load that reads it)
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds), "v"(src)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+                 : "memory", "m0");
 }
 // Same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset.
+template <bool NT>
 __device__ __forceinline__ void lds_load16_at(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(voff),
+                 "s"(sbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -208,20 +224,21 @@ __device__ __forceinline__ uint32_t tile_lane_off(int q, int lane, int64_t strid
 // Rows 4j..4j+3 of a token tile whose row 0 is new token n0 into block j of
 // `tile`.  Rows outside the sequence read 256 bytes of zeros (the padding
 // rows are exact identities of the recurrence).
+template <bool NT>
 __device__ __forceinline__ void load_rows(u16* tile, const u16* src, int64_t stride, const u16* zero,
                                           const Seq& s, int n0, int j, int lane) {
   const int row = 4 * j + (lane >> 4);
   const int n = n0 + row;
   const int k8 = (lane & 15) ^ (row & 15);
   const u16* rp = (unsigned)n < (unsigned)s.L ? src + ((int64_t)s.tok0 + n) * stride : zero;
-  lds_load16(tile + j * 512, rp + k8 * 8);
+  lds_load16<NT>(tile + j * 512, rp + k8 * 8);
 }
 
 // Blocks j0 .. j0 + NB - 1 (j0 a multiple of 4) of a token tile whose row 0
 // is new token n0.  Chunks with every row inside the sequence take uniform
 // bases and the precomputed lane offsets; the first and last chunk of a
 // sequence check rows one by one.
-template <int NB>
+template <int NB, bool NT>
 __device__ __forceinline__ void load_tile(u16* tile, const u16* src, int64_t stride,
                                           const uint32_t (&voff)[4], const u16* zero, const Seq& s,
                                           int n0, int j0, int lane) {
@@ -229,10 +246,10 @@ __device__ __forceinline__ void load_tile(u16* tile, const u16* src, int64_t str
     const char* base = uniform_ptr(src + ((int64_t)s.tok0 + n0 + 4 * j0) * stride);
     const uint32_t lds = lds_addr(tile + j0 * 512);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) lds_load16_at(lds + i * 1024, base + (int64_t)i * 8 * stride, voff[i & 3]);
+    for (int i = 0; i < NB; ++i) lds_load16_at<NT>(lds + i * 1024, base + (int64_t)i * 8 * stride, voff[i & 3]);
   } else {
 #pragma unroll 1
-    for (int i = 0; i < NB; ++i) load_rows(tile, src, stride, zero, s, n0, j0 + i, lane);
+    for (int i = 0; i < NB; ++i) load_rows<NT>(tile, src, stride, zero, s, n0, j0 + i, lane);
   }
 }
 
@@ -308,7 +325,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     uint32_t off[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) off[q] = tile_lane_off(q, lane, stride);
-    load_tile<4>(sm.u.Kb, p.k + (int64_t)s.hq * kDim, stride, off, p.zero_row, s, n0, 4 * wid, lane);
+    load_tile<4, false>(sm.u.Kb, p.k + (int64_t)s.hq * kDim, stride, off, p.zero_row, s, n0, 4 * wid, lane);
   }
   if (wid == 0) {
     const int n = n0 + lane;
@@ -325,10 +342,10 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     }
     const float Glast = __shfl(G, 63, 64);
     float* sc = p.ws_scal + ch * kRecScal;
-    sc[lane] = bet;
-    sc[kChunk + lane] = G;
-    sc[2 * kChunk + lane] = exp2f(G);
-    sc[3 * kChunk + lane] = exp2f(Glast - G);
+    __builtin_nontemporal_store(bet, sc + lane);
+    __builtin_nontemporal_store(G, sc + kChunk + lane);
+    __builtin_nontemporal_store(exp2f(G), sc + 2 * kChunk + lane);
+    __builtin_nontemporal_store(exp2f(Glast - G), sc + 3 * kChunk + lane);
     sm.G[lane] = G;
     sm.B[lane] = bet;
   }
@@ -477,8 +494,9 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     }
     bf16x8 hi, lo;
     split8(vals, hi, lo);
-    *(bf16x8*)(Tw + (f * 64 + lane) * 8) = hi;
-    *(bf16x8*)(Tw + kTFrags * kFragElems + (f * 64 + lane) * 8) = lo;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, hi), (u32x4*)(Tw + (f * 64 + lane) * 8));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, lo),
+                                (u32x4*)(Tw + kTFrags * kFragElems + (f * 64 + lane) * 8));
   }
 }
 
@@ -494,7 +512,7 @@ __device__ __forceinline__ int state_k(int mb, int gq) { return 32 * (mb >> 1) +
 // dst points at the lane's state row (v), k = 0
 __device__ __forceinline__ void store_state(float* dst, const f32x4 (&accS)[8], int gq) {
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) *(f32x4*)(dst + state_k(mb, gq)) = accS[mb];
+  for (int mb = 0; mb < 8; ++mb) __builtin_nontemporal_store(accS[mb], (f32x4*)(dst + state_k(mb, gq)));
 }
 
 // The lane's state row in a caller's state buffer (fp32, or bf16 rounded to
@@ -540,14 +558,15 @@ struct RecSmem {
 
 // Half `part` (0 or 1) of the T fragments of chunk slot c (already in LDS
 // order), with the per-row scalars in half 0.
+template <bool NT>
 __device__ __forceinline__ void load_rec(u16* Tdst, float* sdst, const PrefillParams& p, const Seq& s,
                                          int64_t c, int part, int lane) {
   const int64_t ch = c * p.H + s.h;
   const char* Tw = uniform_ptr(p.ws_T + ch * kRecWords + kTFrags * part * 512);
   const uint32_t lds = lds_addr(Tdst + kTFrags * part * 512);
 #pragma unroll
-  for (int i = 0; i < kTFrags; ++i) lds_load16_at(lds + i * 1024, Tw + i * 1024, lane * 16);
-  if (part == 0) lds_load16_at(lds_addr(sdst), uniform_ptr(p.ws_scal + ch * kRecScal), lane * 16);
+  for (int i = 0; i < kTFrags; ++i) lds_load16_at<NT>(lds + i * 1024, Tw + i * 1024, lane * 16);
+  if (part == 0) lds_load16_at<NT>(lds_addr(sdst), uniform_ptr(p.ws_scal + ch * kRecScal), lane * 16);
 }
 
 // o rows 4j..4j+3 of a finished chunk (row 0 = new token n0), j = j0 ..
@@ -565,7 +584,7 @@ __device__ __forceinline__ void write_o_tile(const PrefillParams& p, const RecSm
     const int nn = n0 + row;
     const u32x4 w = *(const u32x4*)&sm.Os[row][seg * 8];
     if ((unsigned)nn < (unsigned)s.L)
-      *(u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + v0 + seg * 8) = w;
+      __builtin_nontemporal_store(w, (u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + v0 + seg * 8));
   }
 }
 
@@ -580,7 +599,7 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
 #pragma unroll
     for (int i = 0; i < NJ; ++i) w[i] = *(const u32x4*)&sm.Os[4 * (j0 + i) + (lane >> 4)][(lane & 15) * 8];
 #pragma unroll
-    for (int i = 0; i < NJ; ++i) *(gptr<u32x4>)(base + i * 4 * rs + vo) = w[i];
+    for (int i = 0; i < NJ; ++i) __builtin_nontemporal_store(w[i], (gptr<u32x4>)(base + i * 4 * rs + vo));
     return;
   }
 #pragma unroll
@@ -589,7 +608,7 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
     const int nn = n0 + row;
     const u32x4 w = *(const u32x4*)&sm.Os[row][seg * 8];  // pitch keeps 16-byte alignment
     if ((unsigned)nn < (unsigned)s.L)
-      *(u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + seg * 8) = w;
+      __builtin_nontemporal_store(w, (u32x4*)(p.o + (((int64_t)s.tok0 + nn) * p.H + s.h) * kDim + seg * 8));
   }
 }
 
@@ -668,13 +687,13 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   // chunk 0's inputs
 #pragma unroll 1
   for (int j = wid; j < 16; j += NW) {
-    load_rows(sm.Kb[0], ksrc, qk_stride, p.zero_row, s, nbase, j, lane);
-    if (outs) load_rows(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, j, lane);
-    if (!vzero) load_rows(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, j, lane);
+    load_rows<OUT>(sm.Kb[0], ksrc, qk_stride, p.zero_row, s, nbase, j, lane);
+    if (outs) load_rows<OUT>(sm.Qb[0], qsrc, qk_stride, p.zero_row, s, nbase, j, lane);
+    if (!vzero) load_rows<OUT>(sm.Vb, vsrc, v_stride, p.zero_row, s, nbase, j, lane);
   }
   if (vzero)
     for (int i = tid; i < kTileWords / 8; i += kThreads) *(u32x4*)&sm.Vb[8 * i] = u32x4{0u, 0u, 0u, 0u};
-  for (int part = wid; part < 2; part += NW) load_rec(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, part, lane);
+  for (int part = wid; part < 2; part += NW) load_rec<OUT>(sm.Tf[0], &sm.scal[0][0][0], p, s, cs0, part, lane);
 
   f32x4 accS[8];
   if (vzero) {  // the identity: row vrow has its 1 at k = vrow
@@ -744,11 +763,11 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     // and waves 6-7 the next T; after the mid-chunk barrier, waves 0-3 load
     // the next V.
     if constexpr (NW == 8) {
-      if (wid < 2 && more) load_tile<8>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
+      if (wid < 2 && more) load_tile<8, OUT>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * wid, lane);
     } else if (more) {
       // every wave loads 16 / NW consecutive blocks of the next K and Q
-      load_tile<16 / NW>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
-      if (outs) load_tile<16 / NW>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+      load_tile<16 / NW, OUT>(sm.Kb[X ^ 1], ksrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+      if (outs) load_tile<16 / NW, OUT>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
 
     // ---- recurrence: wave w owns state rows 16w..16w+15
@@ -832,16 +851,16 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
         if (ci > 0 && OUT) write_o<8>(p, sm, s, n0 - kChunk, 8 * (wid - 2), lane);
       } else if (more && wid >= 4) {
         if (wid < 6) {
-          if (outs) load_tile<8>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
+          if (outs) load_tile<8, OUT>(sm.Qb[X ^ 1], qsrc, qk_stride, off_qk, p.zero_row, s, n0 + kChunk, 8 * (wid - 4), lane);
         } else {
-          load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid - 6, lane);
+          load_rec<OUT>(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, wid - 6, lane);
         }
       }
     } else {
       if (ci > 0 && OUT) write_o_tile<NW>(p, sm, s, n0 - kChunk, 16 * NW * vt, tid);
       if (more) {
         for (int part = wid; part < 2; part += NW)
-          load_rec(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, part, lane);
+          load_rec<OUT>(sm.Tf[X ^ 1], &sm.scal[X ^ 1][0][0], p, s, (int64_t)cs0 + ci + 1, part, lane);
       }
     }
 
@@ -992,9 +1011,9 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     }
     __syncthreads();  // P and K^T complete; every wave is past its V reads
     if constexpr (NW == 8) {
-      if (more && wid < 4 && !vzero) load_tile<4>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * wid, lane);
+      if (more && wid < 4 && !vzero) load_tile<4, OUT>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, 4 * wid, lane);
     } else if (more && !vzero) {
-      load_tile<16 / NW>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
+      load_tile<16 / NW, OUT>(sm.Vb, vsrc, v_stride, off_v, p.zero_row, s, n0 + kChunk, wid * (16 / NW), lane);
     }
 
     // O^T = scale (S Q^T diag(gamma) + E^T P^T), by 16-token blocks: the
@@ -1439,7 +1458,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int blk = 16 * wid + i;
-      lds_load16_at(dst + blk * (kPairPitch * 4), src + blk * 1024, lane * 16);
+      lds_load16_at<false>(dst + blk * (kPairPitch * 4), src + blk * 1024, lane * 16);
     }
   };
   fetch(0, 0);
