@@ -975,16 +975,22 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
       const int f = bt * 2 + (bs >> 1);
       *(u32x2*)&sm.Pf[(f * 64 + lane) * 8 + 4 * (bs & 1)] = u32x2{f2bf2(v[0], v[1]), f2bf2(v[2], v[3])};
     }
-    // K^T fragments (k block mk = f/2, t-step ks = f%2; with 8 waves, waves
-    // 0-3 take four each: on each SIMD the older wave w of the pair w, w + 4
-    // wins issue, so waves 4-7 set the pace and get less of this work): a K
-    // fragment times the 0/1 operand ksel[mk%2] leaves, in lane (i, g), the
-    // accumulator rows K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of
-    // lane i's A-operand row, 4 consecutive t (exact: one product by 1).
+    // K^T fragments (k block mk = f/2, t-step ks = f%2).  With 8 waves only
+    // waves 0-3 take them (on each SIMD the older wave w of the pair w, w + 4
+    // wins issue, so waves 4-7 set the pace and get less of this work), and
+    // waves 0-1 take six each against two for waves 2-3, which carry the o
+    // stores and the two extra P blocks: f = w, w + 4 for every such wave,
+    // then 8 + w, 12 + w, 10 + w, 14 + w for w < 2.  A K fragment times the
+    // 0/1 operand ksel[mk%2] leaves, in lane (i, g), the accumulator rows
+    // K[16mt + 4g + r][state_k(mk, i/4) + i%4] -- the k of lane i's A-operand
+    // row, 4 consecutive t (exact: one product by 1).
 #pragma unroll
-    for (int i = 0; i < (NW == 8 ? 4 : 16 / NW); ++i) {
-      if (NW == 8 && wid >= 4) break;
-      const int f = NW == 8 ? wid + 4 * i : wid + NW * i;
+    for (int i = 0; i < (NW == 8 ? 6 : 16 / NW); ++i) {
+      if (NW == 8 && (wid >= 4 || (i >= 2 && wid >= 2))) break;
+      const int f = NW != 8 ? wid + NW * i
+                  : i < 2   ? wid + 4 * i
+                  : i < 4   ? 8 + wid + 4 * (i - 2)
+                            : 10 + wid + 4 * (i - 4);
       const int mk = f >> 1, ks = f & 1;
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       const f32x4 c1 = mfma16x16x32(tile_frag(Kb, (2 * ks) * 4 + (mk >> 1), lane), ksel[mk & 1], zero);
