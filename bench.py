@@ -90,6 +90,31 @@ def measured_traffic():
     return {"prefill": int(m.group(2)), "decode": int(m.group(3))}
 
 
+def plain_copy_gbps(torch, mib: int, reps: int = 10, rounds: int = 3, gdn=None) -> float:
+    """GB/s (read + written bytes) of a device copy of `mib` MiB, median over
+    `rounds` of `reps` back-to-back copies timed with events: the library's
+    streaming copy when `gdn` is given, else torch's copy_ (the runtime's
+    device-to-device memcpy)."""
+    n = mib << 20
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    copy = (lambda: gdn.stream_copy(dst, src)) if gdn is not None else (lambda: dst.copy_(src))
+    copy()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(rounds):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            copy()
+        b.record()
+        torch.cuda.synchronize()
+        res.append(2 * n * reps / (a.elapsed_time(b) / 1e3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return sorted(res)[len(res) // 2]
+
+
 # ----------------------------------------------------------------- algorithmic work
 def prefill_bytes(T: int, H: int, Hqk: int, n_state_io: int) -> int:
     """q, k (per q/k head), v, o (bf16) and g, beta (fp32) per token, plus the
@@ -577,20 +602,7 @@ def main():
     torch.manual_seed(0)
     copy_gbps = None
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib << 20
-        src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        reps = 5
-        for _ in range(reps):
-            dst.copy_(src)
-        b.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * n * reps / (a.elapsed_time(b) / 1e3) / 1e9
-        del src, dst
+        copy_gbps = plain_copy_gbps(torch, args.calibrate_copy_mib, reps=5, rounds=1)
     if args.workload != "hybrid":
         print(json.dumps(single(args, torch, gdn, workloads)), flush=True)
         return
@@ -604,6 +616,13 @@ def main():
                          ("config3_long_prefill", measure_config3)):
             side[name], shapes[name] = fn(torch, gdn, workloads)
             torch.cuda.empty_cache()
+        # what plain copies of 1 GiB reach on this GPU (1 GiB read + 1 GiB
+        # written each): the library's streaming copy, which moves bytes the
+        # way the decode does, and the runtime's device-to-device memcpy
+        for name, use_lib in (("stream_copy", True), ("hip_memcpy_d2d", False)):
+            gbps = plain_copy_gbps(torch, 1024, gdn=gdn if use_lib else None)
+            side[name] = {"GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+                          "bytes_per_copy": 2 << 30}
         line["side"] = side
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(shapes, args.layers)

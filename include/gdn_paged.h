@@ -406,6 +406,20 @@ int gdn_csr_to_block_table(const int32_t* page_indptr, const int32_t* page_indic
                            int32_t max_blocks, int32_t* block_tables, int64_t row_stride,
                            int32_t* ctx_lens, int32_t* bad_rows, hipStream_t stream);
 
+/*
+ * gdn_stream_copy -- copies `bytes` bytes from src to dst (device pointers,
+ * 16-byte aligned, not overlapping) on `stream`, with the memory access
+ * pattern of the decode kernel (16-byte non-temporal loads and stores, a
+ * fixed grid of 8 workgroups per compute unit walking 32 KiB units, each
+ * unit's successor loaded before the unit is stored).  Not part of the
+ * method: it gives the rate an HBM-bound kernel of this library can reach on
+ * the GPU at hand, which the benchmark reports beside the decode's.
+ * Errors: GDN_EINVAL for a size that is negative or not a multiple of 16,
+ * null, unaligned or overlapping pointers (bytes == 0 does nothing),
+ * GDN_ELAUNCH.
+ */
+int gdn_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* gdn_last_error(void);
 

@@ -25,5 +25,6 @@ from ._lib import (  # noqa: F401
     prefill_paged_noalloc,
     prefill_slots,
     prefill_workspace_size,
+    stream_copy,
     version,
 )

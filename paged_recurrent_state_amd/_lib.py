@@ -95,7 +95,8 @@ def checked(word: torch.Tensor, num_pages: int, **fields) -> Options:
 
 EXPORTS = ["gdn_check_paged", "gdn_prefill_slots", "gdn_decode_slots", "gdn_prefill_workspace_size",
            "gdn_prefill_paged", "gdn_prefill_paged_noalloc", "gdn_decode_paged", "gdn_prefill", "gdn_decode",
-           "gdn_block_table_to_csr", "gdn_csr_to_block_table", "gdn_last_error", "gdn_version"]
+           "gdn_block_table_to_csr", "gdn_csr_to_block_table", "gdn_stream_copy", "gdn_last_error",
+           "gdn_version"]
 
 
 def lib_path() -> str:
@@ -129,6 +130,7 @@ def load():
                                  I32, P, P]),
         "gdn_block_table_to_csr": (C.c_int, [P, I64, P, I32, I32, I32, P, P, P, P, P]),
         "gdn_csr_to_block_table": (C.c_int, [P, P, P, I32, I32, I32, P, I64, P, P, P]),
+        "gdn_stream_copy": (C.c_int, [P, P, I64, P]),
         "gdn_last_error": (C.c_char_p, []),
         "gdn_version": (C.c_char_p, []),
     }
@@ -286,6 +288,21 @@ def check_paged(page_indices, page_indptr, last_page_len, page_size: int, num_pa
                                _ptr(last_page_len), B, int(page_size), int(num_pages), _ptr(word),
                                _stream(dev)))
     return word
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
+    """Copy ``src`` into ``dst`` (contiguous device tensors of equal byte size,
+    a multiple of 16) with the library's streaming copy kernel; returns dst."""
+    lib = load()
+    if not (dst.is_cuda and src.is_cuda and dst.device == src.device):
+        raise ValueError("dst and src must be tensors on one GPU")
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("dst and src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src differ in size")
+    _check(lib.gdn_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device)))
+    return dst
 
 
 def decode_slots(page_indices, page_indptr, last_page_len,

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn_paged.so")
 
 SOURCES = ["gdn_slots.hip", "gdn_tables.hip", "gdn_check.hip", "gdn_prefill.hip", "gdn_decode.hip",
-           "gdn_api.hip"]
+           "gdn_copy.hip", "gdn_api.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -485,6 +485,19 @@ int gdn_check_paged(const int32_t* cu_seqlens, const int32_t* page_indices,
   return ok();
 }
 
+int gdn_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16)
+    return fail(GDN_EINVAL, "bytes must be a non-negative multiple of 16 (got %lld)", (long long)bytes);
+  if (bytes == 0) return ok();
+  if (!dst || !src) return fail(GDN_EINVAL, "dst and src must not be NULL");
+  if ((uintptr_t)dst % 16 || (uintptr_t)src % 16)
+    return fail(GDN_EINVAL, "dst and src must be 16-byte aligned");
+  const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
+  if (d < s + (uintptr_t)bytes && s < d + (uintptr_t)bytes) return fail(GDN_EINVAL, "dst and src overlap");
+  if (int rc = launched(launch_stream_copy(dst, src, bytes, stream), "copy kernel")) return rc;
+  return ok();
+}
+
 int gdn_prefill_paged(const gdn_dims_t* dims, const void* q, const void* k, const void* v,
                       const float* g, const float* beta, const int32_t* cu_seqlens,
                       int32_t num_seqs, int64_t total_tokens, void* state_pool,

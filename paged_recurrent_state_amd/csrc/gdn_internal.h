@@ -138,6 +138,7 @@ hipError_t launch_prefill_slots(const int32_t* cu, const int32_t* idx, const int
                                 int32_t* chunk_start, const int32_t* guard, hipStream_t s);
 hipError_t launch_decode_slots(const int32_t* idx, const int32_t* ptr, const int32_t* lpl,
                                int B, int32_t* read, int32_t* write, hipStream_t s);
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 hipError_t launch_check_paged(const int32_t* cu, const int32_t* idx, const int32_t* ptr,
                               const int32_t* lpl, int B, int page_size, int num_pages,
                               int32_t* word, hipStream_t s);

@@ -242,3 +242,19 @@ def test_check_rejects_bad_args(lib):
     o = _lib.Options(check_error_word=0x1000, check_num_pages=0)
     assert _prefill_paged(lib, dims(options=o)) == -1
     assert b"check_num_pages" in lib.gdn_last_error()
+
+
+def test_stream_copy_rejects_bad_arguments(lib):
+    """Size, null, alignment and overlap are refused on the host; a zero-byte
+    copy does nothing (no launch)."""
+    EINVAL = -1
+    buf = (C.c_uint8 * 4096)()
+    base = C.addressof(buf) + (-C.addressof(buf)) % 16
+    a, b = C.c_void_p(base), C.c_void_p(base + 1024)
+    assert lib.gdn_stream_copy(a, b, 0, None) == 0
+    assert lib.gdn_stream_copy(a, b, -16, None) == EINVAL
+    assert lib.gdn_stream_copy(a, b, 24, None) == EINVAL
+    assert lib.gdn_stream_copy(None, b, 32, None) == EINVAL
+    assert lib.gdn_stream_copy(C.c_void_p(base + 8), b, 32, None) == EINVAL
+    assert lib.gdn_stream_copy(a, C.c_void_p(base + 512), 1024, None) == EINVAL
+    assert b"overlap" in lib.gdn_last_error()
