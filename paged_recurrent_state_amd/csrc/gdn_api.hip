@@ -4,6 +4,7 @@
 #include "gdn_paged.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -370,15 +371,17 @@ int current_device() {
 }
 
 int device_cus() {
-  static int cus[kMaxDevices] = {0};
+  static std::atomic<int> cus[kMaxDevices];  // 0 until first asked (threads may race: same value)
   const int dev = current_device();
   if (dev < 0 || dev >= kMaxDevices) return 256;
-  if (cus[dev] <= 0) {
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
     int n = 0;
-    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
-                   ? n : 256;
+    c = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+            ? n : 256;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 }  // namespace gdn

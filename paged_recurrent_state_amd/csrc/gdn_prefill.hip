@@ -39,6 +39,8 @@
 //   bf16 in one pass.
 //   The next chunk's tiles load straight from global memory into
 //   double-buffered LDS while the current one computes.
+#include <atomic>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -1552,21 +1554,23 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const PrefillParams p) {
 // The dynamic-LDS limit of a kernel is raised once per device (the
 // attribute belongs to the device's copy of the kernel); idempotent if two
 // threads race.
-static bool raise_lds_limit(const void* fn, int bytes, bool (&done)[kMaxDevices], hipError_t* err) {
+// Once per kernel and device (threads that race here both set it: harmless).
+static bool raise_lds_limit(const void* fn, int bytes, std::atomic<bool> (&done)[kMaxDevices],
+                            hipError_t* err) {
   const int dev = current_device();
-  if (dev >= 0 && dev < kMaxDevices && done[dev]) return true;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return true;
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) {
     *err = e;
     return false;
   }
-  if (dev >= 0 && dev < kMaxDevices) done[dev] = true;
+  if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
   return true;
 }
 
 template <int NW, bool OUT>
 hipError_t launch_rec(const PrefillParams& p, int64_t blocks, hipStream_t s) {
-  static bool done[kMaxDevices] = {};
+  static std::atomic<bool> done[kMaxDevices];
   hipError_t e = hipSuccess;
   if (!raise_lds_limit((const void*)rec_kernel<NW, OUT>, (int)sizeof(RecSmem), done, &e)) return e;
   rec_kernel<NW, OUT><<<(unsigned)blocks, NW * 64, sizeof(RecSmem), s>>>(p);
@@ -1612,7 +1616,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   p1.vcount = p.seg_counts;
   if ((e = rec(p1, p.seg_cap1, false)) != hipSuccess) return e;
   {
-    static bool done[kMaxDevices] = {};
+    static std::atomic<bool> done[kMaxDevices];
     if (!raise_lds_limit((const void*)seg_scan_kernel, (int)sizeof(ScanSmem), done, &e)) return e;
   }
   seg_scan_kernel<<<(unsigned)(((int64_t)p.num_seqs * p.H + 7) / 8 * 64), 256, sizeof(ScanSmem), s>>>(p);

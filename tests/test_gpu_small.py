@@ -501,6 +501,20 @@ def test_prefill_gqa_head_placement(H, Hqk, split, waves):
     print(f"H={H} Hqk={Hqk} split {split} waves {waves}: worst state rel {err:.2e}")
 
 
+@pytest.mark.parametrize("H,Hqk,split,waves", [(32, 8, -1, 8), (32, 8, 2, 4), (64, 8, -1, 8),
+                                               (64, 8, 0, 8)])
+def test_paged_prefill_wide_groups(H, Hqk, split, waves):
+    """Groups of 4 and 8 v-heads per q/k head (32 on 8, 64 on 8), where the
+    prefill kernels place eight q/k heads' groups side by side: forced and
+    device-planned segments, a 4-wave tile, every head checked."""
+    o = opts(prefill_split_chunks=split, prefill_tile_waves=waves)
+    pre, pool = make_case([0, 37, 130], [600, 190, 300], ps=128, H=H, Hqk=Hqk,
+                          seed=H + Hqk + split + waves, g_scale=0.1)
+    _, writes, err = check_paged_prefill(pre, pool, options=o)
+    assert len(writes) >= 4
+    print(f"H={H} Hqk={Hqk} split {split} waves {waves}: worst state rel {err:.2e}")
+
+
 @pytest.mark.parametrize("H,Hqk,split", [(16, 8, -1), (32, 16, 2)])
 def test_general_prefill_gqa_head_placement(H, Hqk, split):
     """The slot-argument call with interior checkpoints (every 100 tokens) on
