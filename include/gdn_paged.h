@@ -88,9 +88,11 @@ enum { GDN_STATE_F32 = 0, GDN_STATE_BF16 = 1 };
  *                         4, 2 or 1 = V-tiles of 64, 32 or 16 state rows.
  *   decode_waves          2, 4, 8 or 16: the one-(sequence, head)-per-workgroup
  *                         decode kernel of that width; 0 = default.
- *   decode_stream_per_cu  streaming decode workgroups per compute unit;
- *                         0 = default (6 for fp32 state, one-pair kernel for
- *                         bf16), -1 = the one-pair kernel.
+ *   decode_stream_per_cu  streaming decode (16 waves) workgroups per compute
+ *                         unit; -1 = the one-pair kernel; 0 = default: 6 for
+ *                         fp32 state; for bf16 state (with the two other
+ *                         decode fields 0) the streaming kernel with 4 waves
+ *                         and one workgroup per (sequence, head).
  *   decode_stream_grid    > 0: streaming decode with exactly this many
  *                         workgroups (overrides decode_stream_per_cu).
  */

@@ -256,12 +256,19 @@ hipError_t launch_decode_nw(const DecodeParams& p, unsigned blocks, hipStream_t 
 // unit, 6.0 TB/s on the hybrid step's decode batch (the one-pair kernel: 5.6;
 // 1-12 per unit: 5.75-6.0); the extra workgroups beyond the resident ones
 // even out the walk's tail.  bf16 pools (half the bytes a pair): the
-// one-pair kernel with 16 waves, 5.5 TB/s (streaming: 4.4-4.6).  One-pair
-// kernels with 4, 2 or 8 waves ran at 5.2-5.5.  The shape arguments pick
-// another (tests, tuning); every choice gives bit-identical results.
+// walking kernel with 4 waves and a grid of one workgroup per pair, 5.6
+// TB/s; its compiled form keeps a pair's 8 row loads a lane in flight in 175
+// VGPRs, 2 workgroups per compute unit (the one-pair kernel: 5.3 with 16
+// waves, 5.1-5.4 with 4 or 8; streaming with fewer workgroups than pairs:
+// 4.9-5.3).  The shape arguments pick another (tests, tuning); every choice
+// gives bit-identical results.
 hipError_t launch_decode(const DecodeParams& p, const DecodeShape& shape, hipStream_t s) {
   const int64_t blocks = (int64_t)p.num_seqs * p.H;
   if (blocks <= 0) return hipSuccess;
+  if (p.state_bf16 && shape.waves == 0 && shape.stream_per_cu == 0 && shape.stream_grid == 0) {
+    decode_stream_kernel<true, 4><<<(unsigned)blocks, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
   // a one-pair width asked for alone selects the one-pair kernel
   int per_cu = p.state_bf16 || shape.waves ? 0 : 6;
   if (shape.stream_per_cu > 0) per_cu = shape.stream_per_cu;
