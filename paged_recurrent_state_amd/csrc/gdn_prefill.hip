@@ -512,9 +512,15 @@ constexpr int kOsPitch = kDim + 8;  // bf16 row pitch of the output tile
 __device__ __forceinline__ int state_k(int mb, int gq) { return 32 * (mb >> 1) + 8 * gq + 4 * (mb & 1); }
 
 // dst points at the lane's state row (v), k = 0
+// (NT: non-temporal, for rows the caller reads later; the workspace states
+// the next kernel of the call reads keep the default policy)
+template <bool NT = true>
 __device__ __forceinline__ void store_state(float* dst, const f32x4 (&accS)[8], int gq) {
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) __builtin_nontemporal_store(accS[mb], (f32x4*)(dst + state_k(mb, gq)));
+  for (int mb = 0; mb < 8; ++mb) {
+    if constexpr (NT) __builtin_nontemporal_store(accS[mb], (f32x4*)(dst + state_k(mb, gq)));
+    else *(f32x4*)(dst + state_k(mb, gq)) = accS[mb];
+  }
 }
 
 // The lane's state row in a caller's state buffer (fp32, or bf16 rounded to
@@ -1123,7 +1129,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
     else write_o_tile<NW>(p, sm, s, nbase + kChunk * (nch - 1), 16 * NW * vt, tid);
   }
   if (wr >= 0 && p.out) store_state_buf(p.out, (int64_t)wr * p.out_stride + head_off, accS, gq, p.state_bf16);
-  if (wr <= -2) store_state(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, accS, gq);
+  if (wr <= -2) store_state<false>(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, accS, gq);
 }
 
 // Launch plan, one workgroup: the longest-first order of the sequences (by
