@@ -14,9 +14,12 @@ Everything here is plain, slow and meant to be read against the pages:
   prefill/decode and the paged wrappers.
 
 Pins (see ``tests/test_oracle_*.py``): the worked examples the pages print,
-closed forms, special cases and brute force on tiny inputs.  Random-input
-numerics beyond those are "parity unpinned": the pages print no output or
-state values, so this oracle is the only reference for them.
+closed forms, special cases and brute force on tiny inputs; every function
+here is held by at least one of them.  The pages print no output or state
+values, so on random inputs the recurrence is held by the closed form (an
+independent product of per-token maps, on random inputs with small heads) and
+by invariants (split invariance, linearity in the start state, decode as a
+one-token prefill) rather than by printed numbers.
 """
 
 from . import csr, slots, gdn  # noqa: F401
