@@ -116,3 +116,29 @@ def test_plan_records(split):
     assert split_any, "the plan cut no sequence"
     print(f"split {split}: {n1} first-pass and {n2} second-pass records; segments per "
           f"sequence {[int(x[0]) for x in scan]}")
+
+
+@pytest.mark.parametrize("g_scale", [1.0, 0.1])
+def test_auto_plan_one_long_head(g_scale):
+    """One sequence on one head, 40,000 new tokens after a prefix that ends
+    inside a page: the device plan may cut it into hundreds of segments (its
+    room is min(chunks / 4 + B, 512 / H + B)); outputs, every page-boundary
+    state and the final state against the oracle."""
+    from tests.test_gpu_small import check_paged_prefill
+    pre, pool = make_case([100], [40000], ps=1024, H=1, Hqk=1, seed=91, g_scale=g_scale)
+    _, writes, err = check_paged_prefill(pre, pool, options=opts(prefill_split_chunks=0))
+    assert len(writes) == 40
+    print(f"g x {g_scale}: {len(writes)} rows written, worst state rel {err:.2e}")
+
+
+def test_auto_plan_at_the_pair_limit():
+    """128 sequences on 2 heads (B * H = 256, the most the device plan takes),
+    ragged lengths with a few long ones."""
+    from tests.test_gpu_small import check_paged_prefill
+    rng = np.random.default_rng(17)
+    new = [int(x) for x in rng.integers(1, 200, 128)]
+    new[3], new[70], new[101] = 3000, 2200, 1500
+    prefix = [int(x) for x in rng.integers(0, 300, 128)]
+    pre, pool = make_case(prefix, new, ps=128, H=2, Hqk=1, seed=92, g_scale=0.3)
+    _, writes, err = check_paged_prefill(pre, pool, options=opts(prefill_split_chunks=0))
+    print(f"{len(writes)} rows written, worst state rel {err:.2e}")
