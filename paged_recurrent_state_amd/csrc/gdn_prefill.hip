@@ -624,8 +624,11 @@ __device__ __forceinline__ void write_o(const PrefillParams& p, const RecSmem& s
 // OUT: the run produces outputs, checkpoints and its final state (whole
 // sequences, and the sequence-parallel second pass); without, it is a
 // first-pass segment run (offset or transition) that only ends in a state.
-template <int NW, bool OUT>
-__global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
+// ROLE (8 waves): the wave pair 2 ROLE, 2 ROLE + 1 this copy of the body
+// runs for, wsel the wave within the pair; -1 (narrower tiles): wsel is
+// the wave index.
+template <int NW, bool OUT, int ROLE>
+__device__ __forceinline__ void rec_body(const PrefillParams& p, int wsel) {
   constexpr int kThreads = NW * 64;
   constexpr int kTiles = 8 / NW;  // V-tiles per head
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   if (guarded(p.guard)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
+  const int wid = ROLE >= 0 ? 2 * ROLE + wsel : wsel;  // wave index (its pair compile-time)
   const int n16 = lane & 15, gq = lane >> 4;
 
   // Longest sequences first: blockIdx walks p.order (sorted by chunk count);
@@ -1130,6 +1133,28 @@ __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   }
   if (wr >= 0 && p.out) store_state_buf(p.out, (int64_t)wr * p.out_stride + head_off, accS, gq, p.state_bf16);
   if (wr <= -2) store_state<false>(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, accS, gq);
+}
+
+// With 8 waves the pairs (0, 1), (2, 3), (4, 5), (6, 7) have different work
+// (loads, o stores, P blocks, K^T fragments), so each pair runs its own copy
+// of the body, compiled with the pair known: its role tests fold away and
+// its block and fragment offsets become constants, which takes vector
+// compares, address arithmetic and scalar spills out of every chunk (4
+// copies: one per wave measured slower, the code then outgrows the
+// instruction cache).
+template <int NW, bool OUT>
+__global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (NW == 8) {
+    switch (w >> 1) {
+      case 0: rec_body<NW, OUT, 0>(p, w & 1); break;
+      case 1: rec_body<NW, OUT, 1>(p, w & 1); break;
+      case 2: rec_body<NW, OUT, 2>(p, w & 1); break;
+      default: rec_body<NW, OUT, 3>(p, w & 1); break;
+    }
+  } else {
+    rec_body<NW, OUT, -1>(p, w);
+  }
 }
 
 // Launch plan, one workgroup: the longest-first order of the sequences (by
