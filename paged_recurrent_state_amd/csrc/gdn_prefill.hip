@@ -293,8 +293,8 @@ struct WySmem {
   float B[kChunk];           // beta (0 on padding rows)
 };
 
-__global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
-  __shared__ __align__(16) WySmem sm;
+template <int W>
+__device__ __forceinline__ void wy_body(const PrefillParams& p, WySmem& sm) {
   if (guarded(p.guard)) return;
   // Workgroups go to the 8 XCDs round-robin by block index: block b runs on
   // XCD b % 8, and every v-head of chunk slot c runs on XCD c % 8, so the
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
   const int h = r - cg * p.H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
+  const int wid = W;
   const int n16 = lane & 15, gq = lane >> 4;
 
   const int4 e = p.chunk_tab[c];  // the same for every lane
@@ -499,6 +499,19 @@ __global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, hi), (u32x4*)(Tw + (f * 64 + lane) * 8));
     __builtin_nontemporal_store(__builtin_bit_cast(u32x4, lo),
                                 (u32x4*)(Tw + kTFrags * kFragElems + (f * 64 + lane) * 8));
+  }
+}
+
+// Each of the four waves runs its own compiled copy of the body (its K K^T
+// blocks, substitution and doubling steps then have constant offsets):
+// 1.5% less time than one copy with a run-time wave index.
+__global__ __launch_bounds__(kWyThreads) void wy_kernel(const PrefillParams p) {
+  __shared__ __align__(16) WySmem sm;
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: wy_body<0>(p, sm); break;
+    case 1: wy_body<1>(p, sm); break;
+    case 2: wy_body<2>(p, sm); break;
+    default: wy_body<3>(p, sm); break;
   }
 }
 
