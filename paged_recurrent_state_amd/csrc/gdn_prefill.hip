@@ -1153,8 +1153,7 @@ __device__ __forceinline__ void rec_body(const PrefillParams& p, int wsel) {
 // of the body, compiled with the pair known: its role tests fold away and
 // its block and fragment offsets become constants, which takes vector
 // compares, address arithmetic and scalar spills out of every chunk (4
-// copies: one per wave measured slower, the code then outgrows the
-// instruction cache).
+// copies; one copy per wave, twice the code, measured slower).
 template <int NW, bool OUT>
 __global__ __launch_bounds__(NW * 64) void rec_kernel(const PrefillParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
