@@ -56,7 +56,7 @@ struct WsLayout {
   int64_t nc;
   int split_mode, split_m;
   int64_t cap1, cap2, rows;
-  size_t slots, order, zero, tab, T, scal, seg1, seg2, scan, counts, states, total;
+  size_t slots, order, zero, tab, T, scal, seg1, seg2, scan, counts, states, bound, total;
 };
 
 // Launch choices of a call, from dims->options (NULL: all defaults).
@@ -137,7 +137,7 @@ WsLayout ws_layout(int64_t T, int B, int H, int split_opt, bool bound = false) {
   off += align256((size_t)w.nc * H * kRecWords * sizeof(u16));
   w.scal = off;
   off += align256((size_t)w.nc * H * kRecScal * sizeof(float));
-  w.seg1 = w.seg2 = w.scan = w.counts = w.states = off;
+  w.seg1 = w.seg2 = w.scan = w.counts = w.states = w.bound = off;
   if (segs > 0) {
     w.seg1 = off;
     off += align256((size_t)w.cap1 * kSegWords * sizeof(int32_t));
@@ -149,6 +149,8 @@ WsLayout ws_layout(int64_t T, int B, int H, int split_opt, bool bound = false) {
     off += 256;
     w.states = off;
     off += align256((size_t)w.rows * H * kDim * kDim * sizeof(float));
+    w.bound = off;  // one float per (chunk slot, v-head)
+    off += align256((size_t)w.nc * H * sizeof(float));
   }
   w.total = off;
   return w;
@@ -263,6 +265,7 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.seg_counts = (int32_t*)((char*)ws + L.counts);
   pp.ws_state = (float*)((char*)ws + L.states);
   pp.ws_state_stride = (int64_t)d->num_v_heads * kDim * kDim;
+  pp.ws_bound = L.split_mode != kSplitOff ? (float*)((char*)ws + L.bound) : nullptr;
   pp.vseq = nullptr;
   pp.vcount = nullptr;
   pp.guard = guard;

@@ -95,6 +95,8 @@ struct PrefillParams {
   int4* seg_scan;          // [B] {segments, first workspace state row, -, -}
   int32_t* seg_counts;     // [2] records in each pass
   float* ws_state;         // workspace states, rows of H * V * K floats
+  float* ws_bound;         // [chunk slots][H] log2 bound on the norm of each chunk's transition
+                           // (sequence-parallel calls; null otherwise)
   int64_t ws_state_stride;
   const int32_t* vseq;     // the records this launch walks (null: whole sequences)
   const int32_t* vcount;   // how many of them are real

@@ -50,6 +50,10 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 // chunk decay exp(G_last) above which Y = K S^T takes a second (lo) pass
 constexpr float kYLoGamma = 0x1p-10f;
+// A first-pass transition M whose spectral norm is below 2^-300 leaves no
+// trace on a start state: a state's Frobenius norm is below 2^135 in fp32,
+// so start * M is below 2^-165, under the smallest fp32 denormal.
+constexpr float kSkipLog2 = -300.f;
 constexpr int kTileWords = 4 * 4 * kFragElems;  // 64 x 128 bf16, fragment order
 constexpr int kKtWordsL = 8 * 2 * kFragElems;   // K^T fragments
 constexpr int kMatFrag = 8 * kFragElems;        // one 64x64 operand (8 fragments)
@@ -291,6 +295,7 @@ struct WySmem {
   } u;                       // (X = A[32:64, 0:32] T[0:32, 0:32] goes over the A blocks it consumes)
   float G[kChunk];           // log2-scale running decay sum
   float B[kChunk];           // beta (0 on padding rows)
+  float kn[kChunk];          // k.k of each row (the diagonal of K K^T)
 };
 
 template <int W>
@@ -384,10 +389,24 @@ __device__ __forceinline__ void wy_body(const PrefillParams& p, WySmem& sm) {
         const int row = 16 * bi + 4 * gq + r;
         const float val = br[r] * __builtin_amdgcn_exp2f(Gr[r] - Gc) * kk[i][r];
         sm.u.AT[blk][4 * gq + r][n16] = row > col ? val : 0.f;
+        if (bi == bj && row == col) sm.kn[row] = kk[i][r];
       }
     }
   }
   __syncthreads();
+
+  // For the sequence-parallel first pass: a bound on log2 of the spectral
+  // norm of the chunk's transition prod_t alpha_t (I - beta_t k_t k_t^T),
+  // sum_t (log2 alpha_t + log2 max(1, |1 - beta_t k_t.k_t|)) (the eigenvalues
+  // of I - beta k k^T are 1 and 1 - beta k.k).  Wave 1, idle during the
+  // substitution below, computes it.
+  if (wid == 1 && p.ws_bound) {
+    const float x = fabsf(1.f - sm.B[lane] * sm.kn[lane]);
+    float f = __builtin_amdgcn_logf(fmaxf(1.f, x)) + (x - x);  // log2; + NaN when x is NaN or inf
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) f += __shfl_xor(f, off, 64);
+    if (lane == 0) p.ws_bound[ch] = f + sm.G[kChunk - 1];
+  }
 
   // diagonal 16x16 blocks of (I + A)^-1 by forward substitution, all four in
   // wave 0: lane group d solves block d, one column a lane
@@ -686,6 +705,54 @@ __device__ __forceinline__ void rec_body(const PrefillParams& p, int wsel) {
     ck_base = p.ckpt_idx ? p.slots.ckpt_start[b] : 0;
   }
   if (s.L <= 0) return;  // a zero-length sequence writes nothing
+  // First-pass runs with the chunks' transition bounds at hand (log2 of the
+  // norm of prod_t alpha_t (I - beta_t k_t k_t^T), one per chunk and head):
+  // a transition run whose whole bound is below kSkipLog2 stores zeros; an
+  // offset run starts from zero at the latest chunk from which the rest of
+  // the segment's bound is below it (what came before is wiped out at fp32
+  // resolution), instead of at the segment's first chunk.  A NaN anywhere
+  // makes the bound NaN, and nothing is skipped.
+  bool map_is_zero = false;
+  if constexpr (!OUT) {
+    if (p.ws_bound && mode != kSegNormal) {
+      const int c_all = chunks_of(pre, s.L);
+      const float* bnd = p.ws_bound + (int64_t)cs0 * p.H + s.h;
+      if (mode == kSegMap) {
+        float t = 0.f;
+        for (int base = 0; base < c_all; base += 64) {
+          float v = base + lane < c_all ? bnd[(int64_t)(base + lane) * p.H] : 0.f;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+          t += v;  // the same in every lane and wave
+        }
+        map_is_zero = __builtin_amdgcn_readfirstlane((int)(t < kSkipLog2)) != 0;
+      } else {
+        int k = 0;  // trailing chunks to run (0: all of them)
+        float carry = 0.f;
+        for (int base = 0; base < c_all && k == 0; base += 64) {
+          const int c = c_all - 1 - (base + lane);
+          float v = c >= 0 ? bnd[(int64_t)c * p.H] : 0.f;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(v, off, 64);
+            if (lane >= off) v += y;
+          }
+          v += carry;  // bound of chunks c .. c_all - 1
+          const uint64_t hit = __ballot(c >= 0 && v < kSkipLog2);
+          if (hit) k = base + __builtin_ctzll(hit) + 1;
+          carry = __shfl(v, 63, 64);
+        }
+        k = __builtin_amdgcn_readfirstlane(k);
+        if (k > 0 && k < c_all) {  // run chunks c_all - k .. c_all - 1 from zero
+          const int a = (pre & ~(kChunk - 1)) - pre + kChunk * (c_all - k);
+          s.tok0 += a;
+          s.L -= a;
+          pre += a;
+          cs0 += c_all - k;
+        }
+      }
+    }
+  }
   s.hq = s.h / p.group;
   const int nch = chunks_of(pre, s.L);
   // a transition-map segment: identity start, v = 0; first-pass runs skip Q
@@ -695,6 +762,11 @@ __device__ __forceinline__ void rec_body(const PrefillParams& p, int wsel) {
   const int vb = vt * NW + wid;  // this wave's 16-row block of the state
   const int vrow = 16 * vb + n16;
   const int64_t head_off = ((int64_t)s.h * kDim + vrow) * kDim;
+  if (map_is_zero) {
+    const f32x4 zeros[8] = {};
+    store_state<false>(p.ws_state + (int64_t)(-2 - wr) * p.ws_state_stride + head_off, zeros, gq);
+    return;
+  }
   const u16* ksrc = p.k + (int64_t)s.hq * kDim;
   const u16* qsrc = p.q + (int64_t)s.hq * kDim;
   const u16* vsrc = p.v + (int64_t)s.h * kDim;

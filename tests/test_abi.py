@@ -71,13 +71,15 @@ def test_workspace_size(lib):
 
 def test_workspace_size_sequence_parallel(lib):
     """Splitting into segments of m chunks adds the records of both passes, the
-    per-sequence scan records and up to 3 segment states per segment, with
-    ceil(c / m) <= (T/64 + 2B + 1) / m + B segments in all."""
+    per-sequence scan records, up to 3 segment states per segment, with
+    ceil(c / m) <= (T/64 + 2B + 1) / m + B segments in all, and one float per
+    (chunk slot, v-head): the bound on each chunk's transition."""
     whole = lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(dims(options=split_opt(-1))))
     al = lambda x: (x + 255) // 256 * 256
     for m in (4, 7):
         segs = 103 // m + 1
-        extra = al(2 * segs * 32) + al(segs * 32) + al(16) + 256 + 3 * segs * 4 * 128 * 128 * 4
+        extra = al(2 * segs * 32) + al(segs * 32) + al(16) + 256 + 3 * segs * 4 * 128 * 128 * 4 \
+            + al(103 * 4 * 4)
         d = dims(options=split_opt(m))
         assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == extra
     # default (the device plans from the lengths): room for the segments of
@@ -85,7 +87,7 @@ def test_workspace_size_sequence_parallel(lib):
     # with B' = min(B, 256/H): min(26, 129) = 26 here
     for d in (dims(), dims(options=split_opt(0))):
         assert lib.gdn_prefill_workspace_size(64 * 100, 1, C.byref(d)) - whole == \
-            al(52 * 32) + al(26 * 32) + al(16) + 256 + 78 * 4 * 128 * 128 * 4
+            al(52 * 32) + al(26 * 32) + al(16) + 256 + 78 * 4 * 128 * 128 * 4 + al(103 * 4 * 4)
     # 8 sequences x 32 heads fill 256 units once: min(1017/4 + 8, 16 + 8) = 24
     # segments; 9 sequences do not split themselves, but a smaller batch within
     # the same sizes may, so the room stays (with a 9-entry scan region)
@@ -94,7 +96,8 @@ def test_workspace_size_sequence_parallel(lib):
     for B in (8, 9):
         w0 = lib.gdn_prefill_workspace_size(64 * 1000, B, C.byref(big0))
         assert lib.gdn_prefill_workspace_size(64 * 1000, B, C.byref(big)) - w0 == \
-            al(48 * 32) + al(24 * 32) + al(B * 16) + 256 + 72 * 32 * 128 * 128 * 4
+            al(48 * 32) + al(24 * 32) + al(B * 16) + 256 + 72 * 32 * 128 * 128 * 4 \
+            + al((1000 + 2 * B + 1) * 32 * 4)
     # too few tokens for a 16-chunk sequence: no sequence-parallel room
     assert lib.gdn_prefill_workspace_size(1023, 1, C.byref(dims())) == \
         lib.gdn_prefill_workspace_size(1023, 1, C.byref(dims(options=split_opt(-1))))
