@@ -268,6 +268,7 @@ int run_prefill(const gdn_dims_t* d, const void* q, const void* k, const void* v
   pp.ws_bound = L.split_mode != kSplitOff ? (float*)((char*)ws + L.bound) : nullptr;
   pp.vseq = nullptr;
   pp.vcount = nullptr;
+  pp.vhalf = 0;
   pp.guard = guard;
   if (int rc = launched(launch_prefill(pp, L.nc, stream), "prefill kernels")) return rc;
   return ok();

@@ -93,13 +93,15 @@ struct PrefillParams {
   int32_t* seg1;           // [seg_cap1][kSegWords] first pass (workspace)
   int32_t* seg2;           // [seg_cap2][kSegWords] second pass (workspace)
   int4* seg_scan;          // [B] {segments, first workspace state row, -, -}
-  int32_t* seg_counts;     // [2] records in each pass
+  int32_t* seg_counts;     // [2] first pass: offset runs (as many transition runs); second pass: runs
   float* ws_state;         // workspace states, rows of H * V * K floats
   float* ws_bound;         // [chunk slots][H] log2 bound on the norm of each chunk's transition
                            // (sequence-parallel calls; null otherwise)
   int64_t ws_state_stride;
   const int32_t* vseq;     // the records this launch walks (null: whole sequences)
   const int32_t* vcount;   // how many of them are real
+  int vhalf;               // > 0: the records are two halves of vhalf (offset runs, then
+                           // transition runs), each with *vcount real ones at its start
   const int32_t* guard;    // debug check word (null: none); nonzero error bits: return at once
 };
 

@@ -684,7 +684,8 @@ __device__ __forceinline__ void rec_body(const PrefillParams& p, int wsel) {
   int pre, cs0, rd, wr, ck_base, mode = kSegNormal;
   if (p.vseq) {
     const int vi = item / per_seq;
-    if (vi >= *p.vcount) return;  // beyond this pass's segments
+    const int ri = p.vhalf > 0 && vi >= p.vhalf ? vi - p.vhalf : vi;  // index within its half
+    if (ri >= *p.vcount) return;  // beyond this pass's segments
     const int32_t* d = p.vseq + kSegWords * vi;
     s.tok0 = d[0];
     s.L = d[1];
@@ -1384,15 +1385,43 @@ __device__ __forceinline__ int balanced_len(int c, int m) {
 // Lane j of every wave evaluates candidate j (the longest sequence in j + 2
 // segments) over the wave's share of the sequences; the shares meet once in
 // LDS, where wave 0 prices the 64 candidates and picks the cheapest.
+// The first pass's cost follows the negligible-transition rule: from 16
+// sampled g of every (sequence, head) the plan estimates each sequence's
+// decay per chunk (its weakest head's, in log2), with which an offset run
+// covers only the chunks the rest of the segment does not wipe out and a
+// transition run of a segment that decays below 2^-330 costs nothing (a
+// margin over the kernels' 2^-300 for the sampling).  Without g, or with the
+// key-norm term the sample cannot see, the estimate only misprices the plan;
+// the kernels decide exactly.
 constexpr int kAutoWaves = 4;
+constexpr int kDecaySamples = 16;
+constexpr float kPlanSkipLog2 = 330.f;
 __device__ int auto_split_m(const PrefillParams& p) {
   __shared__ int cnt[256];
+  __shared__ int dec_bits[256];  // per sequence: decay per chunk (log2, >= 0) as float bits
   __shared__ int part_i[kAutoWaves][6][64];
   __shared__ float part_f[kAutoWaves][64];
   __shared__ int chosen;
   const int B = p.num_seqs, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (B > 256) return 0;
   if (tid < B) cnt[tid] = chunks_of(p.slots.prefix[tid], p.cu_seqlens[tid + 1] - p.cu_seqlens[tid]);
+  if (tid < 256) dec_bits[tid] = __float_as_int(3.0e38f);
+  __syncthreads();
+  if (tid < B * p.H) {  // one (sequence, head) pair a thread
+    const int i = tid / p.H, h = tid - i * p.H;
+    const int t0 = p.cu_seqlens[i], L = p.cu_seqlens[i + 1] - t0;
+    float d = 0.f;
+    if (p.g && L > 0) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kDecaySamples; ++j) {
+        const int t = t0 + (int)((int64_t)L * (2 * j + 1) / (2 * kDecaySamples));
+        sum += p.g[(int64_t)t * p.H + h];
+      }
+      d = fmaxf(0.f, -sum * (float)kChunk * kLog2e / kDecaySamples);  // NaN -> 0
+    }
+    atomicMin(&dec_bits[i], __float_as_int(d));  // non-negative floats order as their bits
+  }
   __syncthreads();
   if (wid < kAutoWaves) {
     int cmax = 0;
@@ -1404,6 +1433,7 @@ __device__ int auto_split_m(const PrefillParams& p) {
     for (int i = wid; i < B; i += kAutoWaves) {
       const int c = cnt[i];  // the same address in every lane: one broadcast read
       if (c <= 0) continue;
+      const float d = __int_as_float(dec_bits[i]);
       const int sl = balanced_len(c, m);
       const int g = (c + sl - 1) / sl;
       sg += g;
@@ -1411,8 +1441,11 @@ __device__ int auto_split_m(const PrefillParams& p) {
       gmax = max(gmax, g);
       p2 = max(p2, sl);
       if (g > 1) {
-        p1 = max(p1, sl);
-        w1 += (float)((g - 1) * sl);
+        // first-pass run lengths: the offset's tail, the transition's whole segment or nothing
+        const int koff = d > 1.f ? min(sl, (int)ceilf(kPlanSkipLog2 / d) + 1) : sl;
+        const int kmap = d * sl > kPlanSkipLog2 ? 0 : sl;
+        p1 = max(p1, max(koff, kmap));
+        w1 += (float)((g - 1) * (koff + kmap));
       }
     }
     part_i[wid][0][lane] = sg;
@@ -1450,7 +1483,7 @@ __device__ int auto_split_m(const PrefillParams& p) {
     const float whole = pass_time(H * nact, H * csum, (float)cmax, P);
     float cost = whole;
     if (m < cmax && sg <= p.seg_cap2 && 2 * sg1 <= p.seg_cap1)
-      cost = kCostPass1 * pass_time(2.f * H * sg1, 2.f * H * w1, (float)p1, P) +
+      cost = kCostPass1 * pass_time(2.f * H * sg1, H * w1, (float)p1, P) +
              kCostScanStep * (gmax - 1) * rounds_scan + pass_time(H * sg, H * csum, (float)p2, P) +
              kCostLaunches;
     // cheapest candidate (ties: the longer segments), whole sequences unless one beats them
@@ -1485,7 +1518,7 @@ __device__ void split_plan(const PrefillParams& p) {
       if (m > 0 && c > 0) mm = p.split_mode == kSplitAuto ? balanced_len(c, m) : m;
       G = L <= 0 ? 0 : m > 0 ? (c + mm - 1) / mm : 1;
     }
-    const int n1 = G > 1 ? 2 * (G - 1) : 0, n2 = G, nrow = G > 1 ? 3 * G - 2 : 0;
+    const int n1 = G > 1 ? G - 1 : 0, n2 = G, nrow = G > 1 ? 3 * G - 2 : 0;
     int t1, t2, trow;
     const int o1 = carry1 + block_exclusive_scan(n1, &t1);
     const int o2 = carry2 + block_exclusive_scan(n2, &t2);
@@ -1501,11 +1534,14 @@ __device__ void split_plan(const PrefillParams& p) {
       auto put = [](int32_t* d, int a, int b_, int c, int e, int f, int g_, int h, int i) {
         d[0] = a; d[1] = b_; d[2] = c; d[3] = e; d[4] = f; d[5] = g_; d[6] = h; d[7] = i;
       };
+      // offset runs in the first half of the first pass's records, transition
+      // runs in the second: the offsets, which do the work, are dispatched first
+      const int half = p.seg_cap1 / 2;
       for (int g = 0; g <= G - 2; ++g) {
         const int a = lo(g), n = hi(g) - a;
-        put(p.seg1 + kSegWords * (o1 + 2 * g), tok0 + a, n, pre + a, cs + g * mm, -1,
+        put(p.seg1 + kSegWords * (o1 + g), tok0 + a, n, pre + a, cs + g * mm, -1,
             -2 - (row0 + G + g), 0, kSegOffset);
-        put(p.seg1 + kSegWords * (o1 + 2 * g + 1), tok0 + a, n, pre + a, cs + g * mm, -1,
+        put(p.seg1 + kSegWords * (half + o1 + g), tok0 + a, n, pre + a, cs + g * mm, -1,
             -2 - (row0 + 2 * G - 1 + g), 0, kSegMap);
       }
       for (int g = 0; g <= G - 1; ++g) {
@@ -1729,6 +1765,7 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t num_chunk_slots, hipSt
   PrefillParams p1 = p;
   p1.vseq = p.seg1;
   p1.vcount = p.seg_counts;
+  p1.vhalf = p.seg_cap1 / 2;
   if ((e = rec(p1, p.seg_cap1, false)) != hipSuccess) return e;
   {
     static std::atomic<bool> done[kMaxDevices];

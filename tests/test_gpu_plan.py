@@ -2,8 +2,10 @@
 
 White-box: the workspace regions are located as the library lays them out
 (per-sequence rows, launch order, zero row, chunk table, intra-chunk records,
-then the segment records of both passes, the scan records, the counts and the
-segment states, each region 256-byte aligned).  For forced and device-chosen
+then the segment records of both passes -- the first pass's offset runs in the
+first half of its room, its transition runs at the same places in the second
+half -- the scan records, the counts and the segment states, each region
+256-byte aligned).  For forced and device-chosen
 segment lengths the records must:
   * cover every sequence's new tokens exactly, in order, in both passes;
   * never read a caller row in the first pass (zero or identity starts) and,
@@ -70,14 +72,18 @@ def test_plan_records(split):
                     pre["last_page_len"], slots=sl, workspace=ws, options=o)
     torch.cuda.synchronize()
     reg = plan_regions(T, B, H, split, m_forced=split)
-    n1, n2 = read_i32(ws, reg["counts"], 2)
-    rec1 = read_i32(ws, reg["seg1"], 8 * n1).reshape(-1, 8)
+    n1, n2 = read_i32(ws, reg["counts"], 2)  # offset runs (as many transition runs), runs
+    cap1 = 2 * reg["cap"]
+    rec1_all = read_i32(ws, reg["seg1"], 8 * cap1).reshape(-1, 8)
+    off1, map1 = rec1_all[:n1], rec1_all[cap1 // 2:cap1 // 2 + n1]
     rec2 = read_i32(ws, reg["seg2"], 8 * n2).reshape(-1, 8)
     scan = read_i32(ws, reg["scan"], 4 * B).reshape(-1, 4)
     cu = pre["cu_seqlens"].tolist()
     rd = sl.state_indices.tolist()
     wr = sl.output_state_indices.tolist()
-    assert n2 <= reg["cap"] and n1 <= 2 * reg["cap"]
+    assert n2 <= reg["cap"] and n1 <= reg["cap"]
+    assert (off1[:, 7] == 1).all() and (map1[:, 7] == 2).all()  # offset, transition
+    assert (off1[:, :4] == map1[:, :4]).all()  # the same segments
     rows = 0
     i1 = i2 = 0
     split_any = False
@@ -106,15 +112,15 @@ def test_plan_records(split):
         rows += 3 * G - 2
         # every second-pass start is a workspace state: start_g at row0 + g
         assert [int(r[4]) for r in mine2] == [-2 - (row0 + g) for g in range(G)]
-        mine1 = rec1[i1:i1 + 2 * (G - 1)]
-        i1 += 2 * (G - 1)
+        mine1 = np.concatenate([off1[i1:i1 + G - 1], map1[i1:i1 + G - 1]])
+        i1 += G - 1
         assert (mine1[:, 4] == -1).all()          # zero / identity starts
         assert (mine1[:, 5] <= -2).all()          # workspace results only
         assert sorted(-2 - mine1[:, 5].astype(int)) == list(range(row0 + G, row0 + 3 * G - 2))
     assert i1 == n1 and i2 == n2
     assert rows <= 3 * reg["cap"]
     assert split_any, "the plan cut no sequence"
-    print(f"split {split}: {n1} first-pass and {n2} second-pass records; segments per "
+    print(f"split {split}: {n1} offset and {n1} transition runs, {n2} second-pass runs; segments per "
           f"sequence {[int(x[0]) for x in scan]}")
 
 
