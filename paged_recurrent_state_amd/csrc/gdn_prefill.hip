@@ -711,8 +711,11 @@ __device__ __forceinline__ void rec_body(const PrefillParams& p, int wsel) {
   // a transition run whose whole bound is below kSkipLog2 stores zeros; an
   // offset run starts from zero at the latest chunk from which the rest of
   // the segment's bound is below it (what came before is wiped out at fp32
-  // resolution), instead of at the segment's first chunk.  A NaN anywhere
-  // makes the bound NaN, and nothing is skipped.
+  // resolution), instead of at the segment's first chunk.  A NaN or infinity
+  // in g, beta or k makes the bound of its chunk NaN, so no sum through it
+  // counts; v does not enter the bound, so a NaN in v inside chunks an offset
+  // run leaves out does not reach the later states (through the full
+  // recurrence it would).
   bool map_is_zero = false;
   if constexpr (!OUT) {
     if (p.ws_bound && mode != kSegNormal) {
