@@ -72,6 +72,50 @@ def test_random_paged_prefill_grouped_heads(seed):
     print(f"grouped case {seed}: {c} worst state rel {err:.2e}")
 
 
+def draw_wide(seed):
+    """Wider draws: up to 8 sequences of up to 2,500 new tokens, the 896-token
+    page of the hybrid step, head groups up to 16 on 8, decay scales from none
+    to 3x (gamma underflows to zero inside a chunk), every tile width and
+    forced segments of up to 9 chunks (long enough for the first pass to skip
+    negligible transitions)."""
+    rng = np.random.default_rng(77000 + seed)
+    B = int(rng.integers(1, 9))
+    ps = int(rng.choice([64, 128, 192, 256, 896]))
+    H, Hqk = [(1, 1), (2, 1), (2, 2), (4, 2), (4, 4), (8, 4), (16, 8), (8, 8)][int(rng.integers(0, 8))]
+    special = [0, 1, 63, 64, 65, ps - 1, ps, ps + 1]
+    maxnew = int(rng.choice([300, 1200, 2500]))
+    if H >= 8:
+        maxnew = min(maxnew, 1200)
+    prefix = [int(rng.choice(special)) if rng.random() < 0.4 else int(rng.integers(0, 2000))
+              for _ in range(B)]
+    new = [int(rng.choice(special)) if rng.random() < 0.3 else int(rng.integers(0, maxnew))
+           for _ in range(B)]
+    for b in range(B):
+        if prefix[b] + new[b] == 0:
+            prefix[b] = 1
+    g_scale = float(rng.choice([0.0, 0.02, 0.1, 1.0, 1.0, 3.0]))
+    bf16 = bool(rng.random() < 0.25)
+    waves = int(rng.choice([8, 8, 8, 4, 2, 1]))
+    split = int(rng.choice([0, 0, 0, -1, 1, 2, 3, 4, 5, 7, 9]))
+    return dict(prefix=prefix, new=new, ps=ps, H=H, Hqk=Hqk, g_scale=g_scale, bf16=bf16,
+                waves=waves, split=split)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_paged_prefill_wide(seed):
+    import torch
+
+    from tests.test_gpu_small import opts
+    c = draw_wide(seed)
+    pre, pool = make_case(c["prefix"], c["new"], ps=c["ps"], H=c["H"], Hqk=c["Hqk"],
+                          seed=seed, g_scale=c["g_scale"])
+    if c["bf16"]:
+        pool = pool.to(torch.bfloat16)
+    o = opts(prefill_tile_waves=c["waves"], prefill_split_chunks=c["split"])
+    _, _, err = check_paged_prefill(pre, pool, options=o)
+    print(f"wide case {seed}: {c} worst state rel {err:.2e}")
+
+
 def draw_general(seed):
     rng = np.random.default_rng(5000 + seed)
     B = int(rng.integers(1, 6))
