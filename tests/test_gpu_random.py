@@ -1,9 +1,12 @@
-"""Seeded random paged prefill batches against the oracle: batch sizes,
-prefixes and new lengths (zeros, page and chunk boundaries included), page
-sizes, head layouts, decay scales, state types, prefill tile widths and forced
-sequence-parallel splits drawn per case.  The same parity bar as every other
-GPU test: outputs and states within tolerance, page-write set and untouched
-rows bit for bit."""
+"""Seeded random batches against the oracle: paged prefill (batch sizes,
+prefixes and new lengths with zeros, page and chunk boundaries, page sizes,
+head layouts, decay scales, state types, prefill tile widths and forced
+sequence-parallel splits drawn per case), the slot-argument prefill, and paged
+decode over every kernel shape.  The same parity bar as every other GPU test:
+outputs and states within tolerance, write sets and untouched rows bit for
+bit."""
+
+import os
 
 import numpy as np
 import pytest
@@ -11,6 +14,12 @@ import pytest
 from tests.test_gpu_small import check_paged_prefill, make_case
 
 pytestmark = pytest.mark.gpu
+
+
+def seeds(n):
+    """The first n seeds, times GDN_RANDOM_SCALE when set (a longer sweep over
+    the same draws, e.g. GDN_RANDOM_SCALE=100)."""
+    return range(n * max(1, int(os.environ.get("GDN_RANDOM_SCALE", "1"))))
 
 
 def draw_case(seed):
@@ -34,7 +43,7 @@ def draw_case(seed):
                 waves=waves, split=split)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", seeds(16))
 def test_random_paged_prefill(seed):
     import torch
 
@@ -49,7 +58,7 @@ def test_random_paged_prefill(seed):
     print(f"case {seed}: {c} worst state rel {err:.2e}")
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", seeds(6))
 def test_random_paged_prefill_grouped_heads(seed):
     """Random draws on head layouts whose v-heads the prefill kernels place in
     q/k-head groups (16 on 8, 32 on 16), shorter sequences."""
@@ -101,7 +110,7 @@ def draw_wide(seed):
                 waves=waves, split=split)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", seeds(24))
 def test_random_paged_prefill_wide(seed):
     import torch
 
@@ -133,7 +142,7 @@ def draw_general(seed):
                 scale=None if rng.random() < 0.7 else 0.05, rng=rng)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", seeds(12))
 def test_random_general_prefill(seed):
     """The slot-argument call with three separate state buffers, random -1
     rows (zero start, skipped final or checkpoint store), int32 or int64 rows,
@@ -195,3 +204,52 @@ def test_random_general_prefill(seed):
         check_state(ck[r], s, f"checkpoint row {r}")
     print(f"general case {seed}: B={B} H={H}/{Hqk} N={N} prefix={c['prefix']} new={c['new']} "
           f"finals={len(res.final)} checkpoints={len(res.checkpoints)}")
+
+
+DECODE_SHAPES = [dict(), dict(decode_waves=2), dict(decode_waves=4), dict(decode_waves=8),
+                 dict(decode_waves=16), dict(decode_stream_per_cu=1), dict(decode_stream_per_cu=6),
+                 dict(decode_stream_grid=3), dict(decode_stream_grid=37)]
+
+
+@pytest.mark.parametrize("seed", seeds(12))
+def test_random_paged_decode(seed):
+    """Random paged decode batches (1-39 sequences, head layouts up to 16 on 8,
+    contexts of 2 to 33,000 tokens, a random share opening a new page, decay
+    from none to 3x) with a random kernel shape, slots derived or passed, on
+    fp32 and bf16 pools: outputs, states, write set and untouched rows."""
+    import torch
+
+    import workloads
+    from oracle import gdn as ogdn
+    from tests.gpu_util import RowView, changed_rows, check_outputs, check_state, cuda, pool_rows_cpu
+    from tests.test_gpu_small import lib, opts, state_dtype_of
+
+    m = lib()
+    rng = np.random.default_rng(9000 + seed)
+    B = int(rng.integers(1, 40))
+    Hqk, H = [(1, 1), (1, 2), (2, 4), (4, 4), (2, 8), (8, 16)][int(rng.integers(0, 6))]
+    nps = int(rng.integers(0, B + 1))
+    c = cuda(workloads.config2(num_seqs=B, qk_heads=Hqk, v_heads=H, num_pages=B * 34 + 8,
+                               new_page_seqs=nps, seed=500 + seed, ctx_lo=2, ctx_hi=33000,
+                               g_scale=float(rng.choice([0.0, 0.1, 1.0, 3.0]))))
+    dec = c["decode"]
+    shape = DECODE_SHAPES[int(rng.integers(0, len(DECODE_SHAPES)))]
+    for pool in (c["pool"], c["pool"].to(torch.bfloat16)):
+        rows_in = pool_rows_cpu(pool, dec["read_rows"])
+        before = pool.clone()
+        sl = (m.decode_slots(dec["page_indices"], dec["page_indptr"], dec["last_page_len"])
+              if rng.random() < 0.5 else None)
+        o = m.decode_paged(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], pool,
+                           dec["page_indices"], dec["page_indptr"], 1024, dec["last_page_len"],
+                           slots=sl, options=opts(**shape))
+        torch.cuda.synchronize()
+        o_ref, writes, _ = ogdn.decode_paged(dec["q"].cpu(), dec["k"].cpu(), dec["v"].cpu(),
+                                             dec["g"].cpu(), dec["beta"].cpu(), RowView(rows_in),
+                                             dec["page_indices"].cpu(), dec["page_indptr"].cpu(),
+                                             dec["last_page_len"].cpu(),
+                                             state_dtype=state_dtype_of(pool))
+        check_outputs(o, o_ref)
+        assert changed_rows(before, pool) == sorted(writes)
+        for r, s in writes.items():
+            check_state(pool[r], s)
+    print(f"decode case {seed}: B={B} H={H}/{Hqk} new-page={nps} {shape}")
