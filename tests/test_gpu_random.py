@@ -1,8 +1,8 @@
 """Seeded random batches against the oracle: paged prefill (batch sizes,
 prefixes and new lengths with zeros, page and chunk boundaries, page sizes,
 head layouts, decay scales, state types, prefill tile widths and forced
-sequence-parallel splits drawn per case), the slot-argument prefill, and paged
-decode over every kernel shape.  The same parity bar as every other GPU test:
+sequence-parallel splits drawn per case), the slot-argument prefill (with and
+without drawn launch options), and paged decode over every kernel shape.  The same parity bar as every other GPU test:
 outputs and states within tolerance, write sets and untouched rows bit for
 bit."""
 
@@ -148,15 +148,44 @@ def test_random_general_prefill(seed):
     rows (zero start, skipped final or checkpoint store), int32 or int64 rows,
     any checkpoint interval and an explicit scale, against the oracle; every
     row no sequence writes keeps its NaN bits."""
+    run_general(draw_general(seed), seed)
+
+
+def draw_general_wide(seed):
+    """Longer sequences (up to 2,500 new tokens), head groups up to 16 on 8,
+    checkpoint intervals up to the 896-token page, and a drawn tile width and
+    sequence-parallel choice (device-planned, whole, or forced segments)."""
+    rng = np.random.default_rng(6000 + seed)
+    B = int(rng.integers(1, 7))
+    H, Hqk = [(1, 1), (2, 1), (4, 2), (8, 4), (16, 8)][int(rng.integers(0, 5))]
+    N = int(rng.choice([1, 48, 64, 100, 128, 200, 896]))
+    max_len = 200 if N == 1 else (1200 if H >= 8 else 2500)
+    special = [0, 1, 63, 64, 65, N - 1, N, N + 1]
+    prefix = [int(rng.choice(special)) if rng.random() < 0.4 else int(rng.integers(0, 3000))
+              for _ in range(B)]
+    new = [min(max_len, int(rng.choice(special)) if rng.random() < 0.3
+               else int(rng.integers(0, max_len + 1))) for _ in range(B)]
+    return dict(B=B, H=H, Hqk=Hqk, N=N, prefix=[max(0, x) for x in prefix],
+                new=[max(0, x) for x in new], g_scale=float(rng.choice([0.0, 0.1, 1.0, 3.0])),
+                bf16=bool(rng.random() < 0.25), idx64=bool(rng.random() < 0.5),
+                scale=None if rng.random() < 0.7 else 0.05, rng=rng,
+                waves=int(rng.choice([8, 8, 4, 2])), split=int(rng.choice([0, 0, -1, 2, 5, 9])))
+
+
+@pytest.mark.parametrize("seed", seeds(12))
+def test_random_general_prefill_wide(seed):
+    run_general(draw_general_wide(seed), seed)
+
+
+def run_general(c, seed):
     import torch
 
     import workloads
     from oracle import gdn as ogdn
     from tests.gpu_util import RowView, changed_rows, check_outputs, check_state, pool_rows_cpu
-    from tests.test_gpu_small import lib
+    from tests.test_gpu_small import lib, opts
 
     m = lib()
-    c = draw_general(seed)
     rng, B, H, Hqk, N = c["rng"], c["B"], c["H"], c["Hqk"], c["N"]
     dev = "cuda"
     gen = workloads.generator(seed)
@@ -180,12 +209,14 @@ def test_random_general_prefill(seed):
     mk = lambda x: torch.tensor(np.asarray(x, dtype=np.int64), dtype=it, device=dev)  # noqa: E731
     rows_in = pool_rows_cpu(init, [r for r in sidx if r >= 0])
     out0, ck0 = out.clone(), ck.clone()
+    options = (opts(prefill_tile_waves=c["waves"], prefill_split_chunks=c["split"])
+               if "split" in c else None)
     o = m.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, initial_state=init,
                   state_indices=mk(sidx), output_state=out, output_state_indices=mk(oidx),
                   output_final_state=True, state_checkpoints=ck,
                   checkpoint_state_indices=mk(cidx if cidx else [0]),
                   checkpoint_cu_starts=mk(ck_start), prefix_lens=mk(c["prefix"]),
-                  checkpoint_every_n_tokens=N, scale=c["scale"])
+                  checkpoint_every_n_tokens=N, scale=c["scale"], options=options)
     torch.cuda.synchronize()
     res = ogdn.prefill(t["q"].cpu(), t["k"].cpu(), t["v"].cpu(), t["g"].cpu(), t["beta"].cpu(),
                        cu.cpu(), initial_state=RowView(rows_in), state_indices=sidx,
@@ -203,8 +234,8 @@ def test_random_general_prefill(seed):
     for r, s in res.checkpoints.items():
         check_state(ck[r], s, f"checkpoint row {r}")
     print(f"general case {seed}: B={B} H={H}/{Hqk} N={N} prefix={c['prefix']} new={c['new']} "
-          f"finals={len(res.final)} checkpoints={len(res.checkpoints)}")
-
+          f"options={(c.get('waves'), c.get('split'))} finals={len(res.final)} "
+          f"checkpoints={len(res.checkpoints)}")
 
 DECODE_SHAPES = [dict(), dict(decode_waves=2), dict(decode_waves=4), dict(decode_waves=8),
                  dict(decode_waves=16), dict(decode_stream_per_cu=1), dict(decode_stream_per_cu=6),
