@@ -104,3 +104,61 @@ def test_value_extremes(case):
     assert o_err <= 3.5e-3 and s_err <= 1e-4
     if case not in ("v_x16", "scale_1"):  # outputs in the configs' range
         assert o_abs <= 2e-2
+
+
+@pytest.mark.parametrize("where", ["g", "beta", "k"])
+@pytest.mark.parametrize("split", [8, -1])
+def test_nan_input_reaches_later_states(where, split):
+    """A NaN in g, beta or k at one token reaches every later output and state
+    of the heads it feeds, as in the recurrence, also when the first pass of
+    the sequence-parallel plan skips work (8-chunk segments with the configs'
+    decay): the token's chunk has a NaN transition bound, so its segment's
+    transition is computed in full and carries the NaN into the next
+    segment's start, even where the offset run starts after the token.
+    Within the token's 64-token chunk the NaN also reaches the rows before it
+    (the chunk's triangular products multiply the zeros above the diagonal by
+    it), and no further back.  Everything else matches the oracle."""
+    def shape(pre, gen):
+        if where == "g":
+            pre["g"][70, 0] = float("nan")
+        elif where == "beta":
+            pre["beta"][70, 0] = float("nan")
+        else:
+            k = pre["k"].clone()
+            k[70, 0, 5] = float("nan")
+            pre["k"] = k
+    pre, pool = paged_case([0], [2048], 256, 2, 1, 91, shape)
+    m = lib()
+    rows_in = pool_rows_cpu(pool, pre["read_rows"])
+    before = pool.clone()
+    o = m.prefill_paged(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], pre["cu_seqlens"],
+                        pool, pre["page_indices"], pre["page_indptr"], pre["page_size"],
+                        pre["last_page_len"], options=opts(prefill_split_chunks=split))
+    torch.cuda.synchronize()
+    o_ref, writes, _ = ogdn.prefill_paged(pre["q"].cpu(), pre["k"].cpu(), pre["v"].cpu(),
+                                          pre["g"].cpu(), pre["beta"].cpu(),
+                                          pre["cu_seqlens"].cpu(), RowView(rows_in),
+                                          pre["page_indices"].cpu(), pre["page_indptr"].cpu(),
+                                          pre["last_page_len"].cpu(), pre["page_size"])
+    og = o.float().cpu().numpy()
+    nan_heads = [0] if where != "k" else [0, 1]  # k: the q/k head feeds both v-heads
+    # outputs: NaN from the token on in the heads it feeds (the oracle), and on
+    # the GPU also from the start of its chunk (token 64), nowhere else
+    ref_nan = np.isnan(o_ref).any(axis=2)
+    got_nan = np.isnan(og).any(axis=2)
+    assert ref_nan[70:, nan_heads].all() and not ref_nan[:70].any()
+    expect = np.zeros_like(ref_nan)
+    expect[64:, nan_heads] = True
+    assert (got_nan == expect).all()
+    fin = ~got_nan
+    assert rel_fro(og[fin], o_ref[fin]) <= 5e-3
+    # states: every stored row after the token is NaN in those heads, finite elsewhere
+    assert changed_rows(before, pool) == sorted(writes)
+    for r, s in writes.items():
+        got = pool[r].float().cpu().numpy()
+        for h in range(2):
+            if np.isnan(s[h]).any():
+                assert h in nan_heads and np.isnan(s[h]).all() and np.isnan(got[h]).all(), (r, h)
+            else:
+                assert np.isfinite(got[h]).all() and rel_fro(got[h], s[h]) <= 1e-3, (r, h)
+    print(f"NaN in {where}, split {split}: {len(writes)} rows stored")
