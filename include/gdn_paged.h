@@ -15,7 +15,12 @@
  * Data layout (row-major, all device memory, all owned by the caller):
  *   q, k         [T, Hqk, K]  bf16 (raw 16-bit patterns)
  *   v            [T, H, V]    bf16
- *   g, beta      [T, H]       fp32 (either may be NULL: g = 0, beta = 1)
+ *   g, beta      [T, H]       fp32 (either may be NULL: g = 0, beta = 1); g
+ *                finite (the chunked prefill takes differences of decay sums
+ *                within a chunk: a reset is a large negative g, not -inf).  A
+ *                NaN in an input reaches at least what the recurrence would
+ *                reach; in the prefill it also reaches the earlier rows of
+ *                its 64-token chunk
  *   o            [T, H, V]    bf16, written for every new token
  *   state pools  [rows, H, V, K] fp32 or bf16 (gdn_dims_t.state_dtype, one type
  *                for every state buffer of a call); each row is one dense
