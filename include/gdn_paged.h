@@ -18,9 +18,12 @@
  *   g, beta      [T, H]       fp32 (either may be NULL: g = 0, beta = 1); g
  *                finite (the chunked prefill takes differences of decay sums
  *                within a chunk: a reset is a large negative g, not -inf).  A
- *                NaN in an input reaches at least what the recurrence would
- *                reach; in the prefill it also reaches the earlier rows of
- *                its 64-token chunk
+ *                NaN in g, beta or k reaches at least what the recurrence
+ *                would reach, and in the prefill also the earlier rows of its
+ *                64-token chunk; a NaN in v reaches the state rows of its
+ *                32-column group, but not the states past the segment it
+ *                sits in when the sequence-parallel first pass leaves its
+ *                chunk out (the chunk's decay then hides it at fp32)
  *   o            [T, H, V]    bf16, written for every new token
  *   state pools  [rows, H, V, K] fp32 or bf16 (gdn_dims_t.state_dtype, one type
  *                for every state buffer of a call); each row is one dense
