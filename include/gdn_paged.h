@@ -23,7 +23,8 @@
  *                64-token chunk; a NaN in v reaches the state rows of its
  *                32-column group, but not the states past the segment it
  *                sits in when the sequence-parallel first pass leaves its
- *                chunk out (the chunk's decay then hides it at fp32)
+ *                chunk out (it may, because for finite v the decay after
+ *                that chunk makes its contribution invisible at fp32)
  *   o            [T, H, V]    bf16, written for every new token
  *   state pools  [rows, H, V, K] fp32 or bf16 (gdn_dims_t.state_dtype, one type
  *                for every state buffer of a call); each row is one dense
