@@ -152,6 +152,9 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _stream(dev: torch.device):
+    if dev.type != "cuda":
+        raise ValueError(f"the tensors are on {dev}: the library runs on the GPU only "
+                         "(it has no CPU path)")
     return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
