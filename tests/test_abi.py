@@ -261,3 +261,43 @@ def test_stream_copy_rejects_bad_arguments(lib):
     assert lib.gdn_stream_copy(C.c_void_p(base + 8), b, 32, None) == EINVAL
     assert lib.gdn_stream_copy(a, C.c_void_p(base + 512), 1024, None) == EINVAL
     assert b"overlap" in lib.gdn_last_error()
+
+
+def test_decode_calls_reject_bad_args(lib):
+    d = dims()
+    f = C.c_void_p(0x1000)  # never dereferenced: every call below fails before launching
+    blk = 4 * 128 * 128
+
+    def paged(B=2, pool=f, stride=blk, ps=128, q=f, o=f):
+        return lib.gdn_decode_paged(C.byref(d), q, f, f, None, None, B, pool, stride, f, f, f,
+                                    ps, None, o, None)
+
+    assert paged(B=-1) == -1
+    assert paged(pool=None) == -1
+    assert paged(stride=blk - 1) == -1
+    assert paged(ps=100) == -1
+    assert paged(q=None) == -1
+    assert paged(o=None) == -1
+    assert paged(B=0) == 0  # an empty batch is a no-op
+
+    def general(B=2, stride=blk, out_state=f, out_idx=f, idx_dtype=0, q=f):
+        return lib.gdn_decode(C.byref(d), q, f, f, None, None, B, f, stride, f, out_state, blk,
+                              out_idx, idx_dtype, f, None)
+
+    assert general(B=-1) == -1
+    assert general(idx_dtype=3) == -1
+    assert general(stride=blk - 1) == -1
+    assert general(out_state=None) == -1  # output_state_indices needs output_state
+    assert general(q=None) == -1
+
+
+def test_noalloc_refuses_calls_beyond_its_scratch(lib):
+    """The fixed-scratch prefill refuses, before touching the device, a call
+    whose workspace would exceed the 256 MiB scratch (here a million tokens on
+    4 heads: ~690 MB of intra-chunk records)."""
+    d = dims()
+    f = C.c_void_p(0x1000)
+    rc = lib.gdn_prefill_paged_noalloc(C.byref(d), f, f, f, None, None, f, 1, 1_000_000, f,
+                                       4 * 128 * 128, f, f, f, 128, None, f, None)
+    assert rc == -4
+    assert b"fixed scratch" in lib.gdn_last_error()
